@@ -1,0 +1,182 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged attention for one AMD MI355X (gfx950).
+ *
+ * Two calls compute attention; the rest are host-only helpers.
+ *
+ *   pkv_decode  one query token per sequence attends every cached token of
+ *               its sequence, reading K and V through a block table, with the
+ *               new token's K/V optionally written in place first.
+ *               Defined by: HF Transformers "paged attention" page, section
+ *               "Jalur decode" (block_table of shape (batch_size,
+ *               max_blocks_per_seq), rows of physical block ids, -1 =
+ *               unallocated, cache_seqlens, one token per sequence, in-place
+ *               cache update); inference-notes "39 · PagedAttention",
+ *               sections 1-3 (one softmax over all scores, exact, partial
+ *               (m, l) results merged as m = max(m1, m2),
+ *               l = l1 e^(m1-m) + l2 e^(m2-m)).
+ *   pkv_varlen  packed variable-length sequences delimited by cumulative
+ *               lengths, no mask: every query row attends every key row of
+ *               its own sequence.  Defined by: HF "paged attention" page,
+ *               section "Jalur Varlen" (cu_seq_lens_q/k, max_length_q/k,
+ *               packed shapes [1, total, heads, head_dim]).
+ *
+ * Conventions shared by every call
+ *  - Every tensor pointer is DEVICE memory owned by the caller, row-major,
+ *    densely packed in the shape given.  The library allocates nothing,
+ *    keeps no state between calls and never synchronises: work is enqueued
+ *    on `stream` (a hipStream_t; NULL = the null stream) and results are
+ *    valid once the caller has synchronised that stream.  Calls on different
+ *    streams may run concurrently; `out` must not alias any input.
+ *  - dtype: PKV_FP32 or PKV_BF16 for q, K, V, new K/V and out alike.
+ *    Arithmetic is fp32 (bf16 products accumulate in fp32); the output is
+ *    rounded to the input dtype (bf16: round to nearest even).
+ *  - Grouped heads: q head h reads kv head h / (num_heads / num_kv_heads);
+ *    num_heads must be a multiple of num_kv_heads.
+ *  - Index tensors are int32.
+ *  - Errors a host check can see (null pointer, bad size, unsupported shape,
+ *    short workspace) return a status and enqueue nothing.  Errors in device
+ *    data (a needed block_table entry that is -1 or >= num_blocks, a
+ *    sequence longer than its table row, a bad cu_seq_lens array, a length
+ *    above max_length_*) cannot be seen without a sync: the kernels never
+ *    read or write out of bounds for them, OR a PKV_ERR_* bit into *err_flag
+ *    (when err_flag is not NULL) and write NaN to that sequence's output.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* null pointer, negative or inconsistent size      */
+  PKV_EUNSUPPORTED = 2,  /* shape or dtype this build has no kernel for       */
+  PKV_EWORKSPACE = 3,    /* workspace NULL or smaller than required           */
+  PKV_EHIP = 4           /* the HIP runtime refused a launch                  */
+} pkv_status;
+
+typedef enum { PKV_FP32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Bits OR-ed into *err_flag by the kernels (sticky: never cleared). */
+#define PKV_ERR_BLOCK 1u   /* a needed block_table entry is -1 or >= num_blocks            */
+#define PKV_ERR_SPAN 2u    /* cache_seqlens < 0, or cached (+ new) tokens exceed the row   */
+#define PKV_ERR_CU 4u      /* cu_seq_lens not 0-based, decreasing, or not ending at total   */
+#define PKV_ERR_MAXLEN 8u  /* a sequence longer than max_length_q / max_length_k            */
+
+/* Text for a status code (static storage, never NULL). */
+const char* pkv_status_string(int status);
+
+/* ABI version of this library (bumped on any signature or layout change). */
+int pkv_abi_version(void);
+
+/*
+ * Host-only validation of pkv_decode's scalar arguments (no device access,
+ * usable without a GPU).  has_new is 1 when k_new/v_new are given.
+ * Supported: head_dim 64 or 128; block_size 16 or 32; num_heads a multiple
+ * of num_kv_heads; partition_tokens 0 (library choice) or a multiple of
+ * block_size no larger than 256 blocks.
+ */
+int pkv_check_decode_args(int dtype, int has_new, int batch, int num_heads, int num_kv_heads,
+                          int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+                          int partition_tokens);
+
+/*
+ * The split-context partition pkv_decode will use for these arguments, in
+ * tokens: either the caller's non-zero partition_tokens, or the library's
+ * choice for 0.  A result >= max_blocks_per_seq * block_size means a single
+ * pass (no partial results, no merge, no workspace).  Returns -1 when
+ * pkv_check_decode_args fails.
+ */
+int pkv_decode_partition_tokens(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_blocks_per_seq, int partition_tokens);
+
+/*
+ * Bytes of device workspace pkv_decode needs: fp32 partial results
+ * (m, l, acc[head_dim]) for every (sequence, q head, partition).  0 for a
+ * single pass.  Returns 0 for arguments pkv_check_decode_args rejects.
+ */
+size_t pkv_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int partition_tokens);
+
+/*
+ * Paged decode attention (HF page "Jalur decode"; inference-notes sections
+ * 1-3).
+ *
+ *   q              [batch, 1, num_heads, head_dim]
+ *   k_cache,       [num_blocks, block_size, num_kv_heads, head_dim]; token u of
+ *   v_cache          physical block pb, kv head g is row (pb*block_size+u)*num_kv_heads+g.
+ *                    Written ONLY at the new tokens' slots.
+ *   block_table    [batch, max_blocks_per_seq] int32; logical block j of
+ *                    sequence i is physical block block_table[i][j]; -1 =
+ *                    unallocated.  Only entries j < ceil(L'_i / block_size)
+ *                    are read (L'_i defined below).  Never modified.
+ *   cache_seqlens  [batch] int32: L_i, tokens cached BEFORE this call.  Never
+ *                    modified (the caller advances it).
+ *   k_new, v_new   [batch, 1, num_kv_heads, head_dim], or both NULL.  When
+ *                    given, sequence i's row is copied bit for bit into slot
+ *                    L_i (logical block L_i / block_size, offset L_i mod
+ *                    block_size; the caller must already have put that block
+ *                    in the table) and is attended: L'_i = L_i + 1.  Without
+ *                    them L'_i = L_i.
+ *   out            [batch, 1, num_heads, head_dim]; L'_i = 0 gives zeros.
+ *   softmax_scale  multiplies q.k before the softmax (1/sqrt(head_dim) usual).
+ *   partition_tokens  split-context partition length in tokens (0 = library
+ *                    choice, see pkv_decode_partition_tokens).  Partitions are
+ *                    fixed logical token ranges; their partial (m, l, acc)
+ *                    are merged by a second kernel.
+ *   workspace      device buffer of at least pkv_decode_workspace_bytes(...)
+ *                    bytes (may be NULL when that is 0).  Scratch only.
+ *   err_flag       device int32, optional (NULL = no reporting); PKV_ERR_* bits.
+ *   stream         hipStream_t.
+ *
+ * Results depend only on logical positions: any placement of the same
+ * logical blocks gives bit-identical output, and repeated calls agree
+ * bitwise.  Two sequences must not append into the same slot.
+ */
+int pkv_decode(int dtype, const void* q, void* k_cache, void* v_cache,
+               const int32_t* block_table, const int32_t* cache_seqlens,
+               const void* k_new, const void* v_new, void* out,
+               int batch, int num_heads, int num_kv_heads, int head_dim,
+               int num_blocks, int block_size, int max_blocks_per_seq,
+               float softmax_scale, int partition_tokens,
+               void* workspace, size_t workspace_bytes,
+               int32_t* err_flag, void* stream);
+
+/*
+ * Host-only validation of pkv_varlen's scalar arguments.  Supported: bf16;
+ * head_dim 64 or 128; num_heads a multiple of num_kv_heads.
+ */
+int pkv_check_varlen_args(int dtype, int batch, int total_q, int total_k, int num_heads,
+                          int num_kv_heads, int head_dim, int max_length_q, int max_length_k);
+
+/*
+ * Variable-length attention over packed sequences, no mask (HF page
+ * "Jalur Varlen").
+ *
+ *   q              [1, total_q, num_heads, head_dim]
+ *   k, v           [1, total_k, num_kv_heads, head_dim]
+ *   cu_seq_lens_q  [batch + 1] int32: query rows of sequence b are
+ *                    cu_seq_lens_q[b] .. cu_seq_lens_q[b+1]-1 (cu[0] = 0,
+ *                    non-decreasing, cu[batch] = total_q).
+ *   cu_seq_lens_k  [batch + 1] int32, the same for key/value rows.
+ *   max_length_q,  upper bounds on the per-sequence lengths; they size the
+ *   max_length_k     launch.  A longer sequence is a data error.
+ *   out            [1, total_q, num_heads, head_dim]; a sequence with no key
+ *                    row outputs zeros.
+ *   err_flag       device int32, optional.
+ */
+int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
+               const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+               int max_length_q, int max_length_k, void* out,
+               int batch, int total_q, int total_k, int num_heads, int num_kv_heads,
+               int head_dim, float softmax_scale, int32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

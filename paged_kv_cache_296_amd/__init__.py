@@ -1,0 +1,224 @@
+"""paged_kv_cache_296_amd -- paged attention on one AMD MI355X (gfx950).
+
+Thin Python binding over ``libpkv.so`` (the C ABI declared in
+``include/pkv.h``).  This module only marshals arguments: it checks tensor
+placement, dtype and shape, allocates outputs and workspace with torch when
+the caller does not pass them, and hands raw device pointers plus the current
+HIP stream to the library.  Every step of the computation runs in the HIP
+kernels; there is no CPU fallback.  If the library is not built, or no GPU is
+visible, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "PkvError", "decode", "varlen", "decode_workspace_bytes", "decode_partition_tokens",
+    "check_decode_args", "check_varlen_args", "status_string", "abi_version", "lib_path",
+    "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
+]
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+FP32, BF16 = 0, 1
+ERR_BLOCK, ERR_SPAN, ERR_CU, ERR_MAXLEN = 1, 2, 4, 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libpkv.so")
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})" if what else
+                         status_string(status))
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is not built; run __graft_entry__.build() "
+                              "(hipcc for gfx950) first")
+        L = ctypes.CDLL(lib_path)
+        P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.pkv_status_string.argtypes = [I]
+        L.pkv_status_string.restype = ctypes.c_char_p
+        L.pkv_abi_version.argtypes = []
+        L.pkv_abi_version.restype = I
+        L.pkv_check_decode_args.argtypes = [I] * 10
+        L.pkv_check_decode_args.restype = I
+        L.pkv_decode_partition_tokens.argtypes = [I] * 7
+        L.pkv_decode_partition_tokens.restype = I
+        L.pkv_decode_workspace_bytes.argtypes = [I] * 7
+        L.pkv_decode_workspace_bytes.restype = SZ
+        L.pkv_decode.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, SZ, P, P]
+        L.pkv_decode.restype = I
+        L.pkv_check_varlen_args.argtypes = [I] * 9
+        L.pkv_check_varlen_args.restype = I
+        L.pkv_varlen.argtypes = [I, P, P, P, P, P, I, I, P, I, I, I, I, I, I, F, P, P]
+        L.pkv_varlen.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _load().pkv_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return _load().pkv_abi_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"paged attention takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU path)")
+
+
+def _need_contig(**ts):
+    for name, t in ts.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def check_decode_args(dtype, has_new, batch, num_heads, num_kv_heads, head_dim, num_blocks,
+                      block_size, max_blocks_per_seq, partition_tokens=0) -> int:
+    return _load().pkv_check_decode_args(int(dtype), int(has_new), batch, num_heads, num_kv_heads,
+                                         head_dim, num_blocks, block_size, max_blocks_per_seq,
+                                         partition_tokens)
+
+
+def check_varlen_args(dtype, batch, total_q, total_k, num_heads, num_kv_heads, head_dim,
+                      max_length_q, max_length_k) -> int:
+    return _load().pkv_check_varlen_args(int(dtype), batch, total_q, total_k, num_heads,
+                                         num_kv_heads, head_dim, max_length_q, max_length_k)
+
+
+def decode_partition_tokens(batch, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, partition_tokens=0) -> int:
+    return _load().pkv_decode_partition_tokens(batch, num_heads, num_kv_heads, head_dim,
+                                               block_size, max_blocks_per_seq, partition_tokens)
+
+
+def decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, partition_tokens=0) -> int:
+    return _load().pkv_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim,
+                                              block_size, max_blocks_per_seq, partition_tokens)
+
+
+def decode(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None, *,
+           softmax_scale=None, partition_tokens=0, out=None, workspace=None, err_flag=None,
+           stream=None):
+    """Paged decode attention; appends k_new/v_new in place when given.
+
+    q [B, 1, Hq, D]; k_cache/v_cache [num_blocks, block_size, Hkv, D];
+    block_table [B, max_blocks] int32; cache_seqlens [B] int32 (before the
+    append, not modified); k_new/v_new [B, 1, Hkv, D] or None.  Returns out
+    [B, 1, Hq, D] in q's dtype.
+    """
+    lib = _load()
+    _need_gpu(q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new, out, workspace,
+              err_flag)
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                 cache_seqlens=cache_seqlens, k_new=k_new, v_new=v_new, out=out)
+    dt = _dtype_code(q)
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [batch, 1, num_heads, head_dim]")
+    B, _, Hq, D = q.shape
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.shape[3] != D:
+        raise ValueError("k_cache/v_cache must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    NB, bs, Hkv, _ = k_cache.shape
+    for t in (k_cache, v_cache, k_new, v_new):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, caches and new K/V must share one dtype")
+    if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
+        raise TypeError("block_table and cache_seqlens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be [batch, max_blocks_per_seq], cache_seqlens [batch]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new or neither")
+    if k_new is not None and (tuple(k_new.shape) != (B, 1, Hkv, D) or k_new.shape != v_new.shape):
+        raise ValueError("k_new/v_new must be [batch, 1, num_kv_heads, head_dim]")
+    maxb = block_table.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rc = lib.pkv_check_decode_args(dt, int(k_new is not None), B, Hq, Hkv, D, NB, bs, maxb,
+                                   int(partition_tokens))
+    if rc:
+        raise PkvError(rc, "pkv_decode arguments")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    need = lib.pkv_decode_workspace_bytes(B, Hq, Hkv, D, bs, maxb, int(partition_tokens))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pkv_decode(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                        _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new), _ptr(out), B, Hq, Hkv, D,
+                        NB, bs, maxb, float(softmax_scale), int(partition_tokens),
+                        _ptr(workspace), wbytes, _ptr(err_flag), _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_decode")
+    return out
+
+
+def varlen(q, k, v, cu_seq_lens_q, cu_seq_lens_k, max_length_q, max_length_k, *,
+           softmax_scale=None, out=None, err_flag=None, stream=None):
+    """Attention over packed sequences, no mask.
+
+    q [1, total_q, Hq, D]; k, v [1, total_k, Hkv, D]; cu_seq_lens_q/k
+    [batch + 1] int32.  Returns out [1, total_q, Hq, D] in q's dtype.
+    """
+    lib = _load()
+    _need_gpu(q, k, v, cu_seq_lens_q, cu_seq_lens_k, out, err_flag)
+    _need_contig(q=q, k=k, v=v, cu_seq_lens_q=cu_seq_lens_q, cu_seq_lens_k=cu_seq_lens_k, out=out)
+    dt = _dtype_code(q)
+    if q.dim() != 4 or q.shape[0] != 1 or k.dim() != 4 or k.shape[0] != 1 or k.shape != v.shape:
+        raise ValueError("q must be [1, total_q, Hq, D] and k, v [1, total_k, Hkv, D]")
+    _, Tq, Hq, D = q.shape
+    _, Tk, Hkv, D2 = k.shape
+    if D2 != D or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share head_dim and dtype")
+    if cu_seq_lens_q.dtype != torch.int32 or cu_seq_lens_k.dtype != torch.int32:
+        raise TypeError("cu_seq_lens_q/k must be int32")
+    if cu_seq_lens_q.dim() != 1 or cu_seq_lens_q.shape != cu_seq_lens_k.shape:
+        raise ValueError("cu_seq_lens_q/k must both be [batch + 1]")
+    B = cu_seq_lens_q.shape[0] - 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rc = lib.pkv_check_varlen_args(dt, B, Tq, Tk, Hq, Hkv, D, int(max_length_q), int(max_length_k))
+    if rc:
+        raise PkvError(rc, "pkv_varlen arguments")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    rc = lib.pkv_varlen(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k),
+                        int(max_length_q), int(max_length_k), _ptr(out), B, Tq, Tk, Hq, Hkv, D,
+                        float(softmax_scale), _ptr(err_flag), _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_varlen")
+    return out

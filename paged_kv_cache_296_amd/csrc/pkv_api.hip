@@ -1,0 +1,239 @@
+// Host entry points of libpkv.so: argument checks, the split-context launch
+// plan, workspace sizing and the launches.  No allocation, no state, no
+// synchronisation (see include/pkv.h for the contract).
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_kernels.h"
+
+namespace {
+
+constexpr int kMaxPartitionBlocks = 256;  // LDS table slice per wave
+constexpr int kAbiVersion = 1;
+
+bool decode_shape_ok(int head_dim, int block_size) {
+  return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+}
+
+// Library choice of partition length: enough (sequence, partition, kv head)
+// units to give every SIMD of the 256 CUs several waves, assuming sequences
+// average half their table span, but at least 256 tokens per unit so the
+// per-unit prologue stays small, and never more than the LDS slice allows.
+int choose_partition(int batch, int num_kv_heads, int head_chunks, int block_size,
+                     int max_blocks_per_seq) {
+  const long long span = (long long)max_blocks_per_seq * block_size;
+  const long long cap = (long long)kMaxPartitionBlocks * block_size;
+  const long long base_units = (long long)batch * num_kv_heads * head_chunks;
+  const long long target_units = 4LL * 1024;  // 4 waves per SIMD on 1024 SIMDs
+  long long p = 256;
+  if (p < block_size) p = block_size;
+  // grow while there are still plenty of units
+  while (p * 2 <= cap && base_units * ((span / 2 + 2 * p - 1) / (2 * p)) >= target_units) p *= 2;
+  if (span <= p && span <= cap) return (int)span;  // a single pass covers every row
+  return (int)p;
+}
+
+struct DecodePlan {
+  int part_tokens;
+  int n_parts;
+  int head_chunks;
+};
+
+int check_decode(int dtype, int has_new, int batch, int num_heads, int num_kv_heads, int head_dim,
+                 int num_blocks, int block_size, int max_blocks_per_seq, int partition_tokens) {
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || partition_tokens < 0 || (has_new != 0 && has_new != 1))
+    return PKV_EINVAL;
+  if (dtype != PKV_FP32 && dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
+  if (!decode_shape_ok(head_dim, block_size)) return PKV_EUNSUPPORTED;
+  if (partition_tokens != 0 &&
+      (partition_tokens % block_size != 0 || partition_tokens / block_size > kMaxPartitionBlocks))
+    return PKV_EUNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX / 2) return PKV_EINVAL;
+  if ((long long)num_blocks * block_size * num_kv_heads * head_dim > (1LL << 46)) return PKV_EINVAL;
+  return PKV_OK;
+}
+
+DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int block_size,
+                       int max_blocks_per_seq, int partition_tokens) {
+  DecodePlan p;
+  const int group = num_heads / num_kv_heads;
+  p.head_chunks = (group + 15) / 16;
+  const long long span = (long long)max_blocks_per_seq * block_size;
+  int pt = partition_tokens != 0
+               ? partition_tokens
+               : choose_partition(batch, num_kv_heads, p.head_chunks, block_size, max_blocks_per_seq);
+  if (pt <= 0) pt = block_size;
+  if (span <= pt) {
+    // one pass; the partition spans the whole row (bounded by the LDS slice)
+    if (span / block_size <= kMaxPartitionBlocks) {
+      p.part_tokens = span > 0 ? (int)span : block_size;
+      p.n_parts = 1;
+      return p;
+    }
+  }
+  p.part_tokens = pt;
+  p.n_parts = (int)((span + pt - 1) / pt);
+  if (p.n_parts < 1) p.n_parts = 1;
+  return p;
+}
+
+size_t workspace_for(const DecodePlan& p, int batch, int num_heads, int head_dim) {
+  if (p.n_parts <= 1) return 0;
+  const size_t slots = (size_t)batch * num_heads * p.n_parts;
+  size_t acc = slots * head_dim * sizeof(float);
+  acc = (acc + 255) & ~(size_t)255;
+  return acc + slots * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported shape or dtype";
+    case PKV_EWORKSPACE: return "workspace missing or too small";
+    case PKV_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_abi_version(void) { return kAbiVersion; }
+
+int pkv_check_decode_args(int dtype, int has_new, int batch, int num_heads, int num_kv_heads,
+                          int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+                          int partition_tokens) {
+  return check_decode(dtype, has_new, batch, num_heads, num_kv_heads, head_dim, num_blocks,
+                      block_size, max_blocks_per_seq, partition_tokens);
+}
+
+int pkv_decode_partition_tokens(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_blocks_per_seq, int partition_tokens) {
+  if (check_decode(PKV_BF16, 0, batch, num_heads, num_kv_heads, head_dim, 1, block_size,
+                   max_blocks_per_seq, partition_tokens) != PKV_OK)
+    return -1;
+  return plan_decode(batch, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                     partition_tokens)
+      .part_tokens;
+}
+
+size_t pkv_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int partition_tokens) {
+  if (check_decode(PKV_BF16, 0, batch, num_heads, num_kv_heads, head_dim, 1, block_size,
+                   max_blocks_per_seq, partition_tokens) != PKV_OK)
+    return 0;
+  DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                             partition_tokens);
+  return workspace_for(p, batch, num_heads, head_dim);
+}
+
+int pkv_decode(int dtype, const void* q, void* k_cache, void* v_cache,
+               const int32_t* block_table, const int32_t* cache_seqlens,
+               const void* k_new, const void* v_new, void* out,
+               int batch, int num_heads, int num_kv_heads, int head_dim,
+               int num_blocks, int block_size, int max_blocks_per_seq,
+               float softmax_scale, int partition_tokens,
+               void* workspace, size_t workspace_bytes,
+               int32_t* err_flag, void* stream) {
+  const int has_new = k_new != nullptr;
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_EINVAL;
+  int rc = check_decode(dtype, has_new, batch, num_heads, num_kv_heads, head_dim, num_blocks,
+                        block_size, max_blocks_per_seq, partition_tokens);
+  if (rc != PKV_OK) return rc;
+  if (!isfinite(softmax_scale)) return PKV_EINVAL;
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return PKV_EINVAL;
+  DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                             partition_tokens);
+  const size_t need = workspace_for(p, batch, num_heads, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_EWORKSPACE;
+
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.cache_seqlens = cache_seqlens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  const size_t slots = (size_t)batch * num_heads * p.n_parts;
+  a.ws_acc = need ? (float*)workspace : nullptr;
+  size_t acc_bytes = (slots * head_dim * sizeof(float) + 255) & ~(size_t)255;
+  a.ws_ml = need ? (float2*)((char*)workspace + acc_bytes) : nullptr;
+  a.err_flag = err_flag;
+  a.batch = batch;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.head_chunks = p.head_chunks;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_tokens = p.part_tokens;
+  a.n_parts = p.n_parts;
+  a.has_new = has_new;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.total_units = (long long)batch * p.n_parts * num_kv_heads * p.head_chunks;
+  if (a.total_units >= (1LL << 31)) return PKV_EUNSUPPORTED;
+  hipError_t e = pkv::launch_decode(dtype, head_dim, block_size, a, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int pkv_check_varlen_args(int dtype, int batch, int total_q, int total_k, int num_heads,
+                          int num_kv_heads, int head_dim, int max_length_q, int max_length_k) {
+  if (batch < 0 || total_q < 0 || total_k < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      max_length_q < 0 || max_length_k < 0)
+    return PKV_EINVAL;
+  if (dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if ((long long)total_q * num_heads * head_dim * 2 > (1LL << 31) * 64) return PKV_EINVAL;
+  if ((long long)total_k * num_kv_heads * head_dim * 2 > (1LL << 31) * 64) return PKV_EINVAL;
+  return PKV_OK;
+}
+
+int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
+               const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+               int max_length_q, int max_length_k, void* out,
+               int batch, int total_q, int total_k, int num_heads, int num_kv_heads,
+               int head_dim, float softmax_scale, int32_t* err_flag, void* stream) {
+  int rc = pkv_check_varlen_args(dtype, batch, total_q, total_k, num_heads, num_kv_heads, head_dim,
+                                 max_length_q, max_length_k);
+  if (rc != PKV_OK) return rc;
+  if (!isfinite(softmax_scale)) return PKV_EINVAL;
+  if (batch == 0 || total_q == 0) return PKV_OK;
+  if (!q || !out || !cu_seq_lens_q || !cu_seq_lens_k || (total_k > 0 && (!k || !v)))
+    return PKV_EINVAL;
+  const int rows = pkv::varlen_rows_per_workgroup();
+  const long long tiles = ((long long)max_length_q + rows - 1) / rows;
+  if (tiles > 65535 || batch > 65535 || num_heads > 65535) return PKV_EUNSUPPORTED;
+  pkv::VarlenArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seq_lens_q;
+  a.cu_k = cu_seq_lens_k;
+  a.out = out;
+  a.err_flag = err_flag;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.max_len_q = max_length_q;
+  a.max_len_k = max_length_k;
+  a.q_tiles = (int)tiles;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = pkv::launch_varlen(dtype, head_dim, a, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the host entry points (pkv_api.hip) and the
+// kernels (decode.hip, varlen.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Everything one decode launch needs; passed by value as the kernel argument.
+struct DecodeArgs {
+  const void* q;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* cache_seqlens;
+  const void* k_new;
+  const void* v_new;
+  void* out;
+  float* ws_acc;      // [batch, num_heads, n_parts, head_dim] unnormalised sums
+  float2* ws_ml;      // [batch, num_heads, n_parts] (running max, sum of exponentials)
+  int32_t* err_flag;  // may be null
+  int batch, num_heads, num_kv_heads, group;  // group = num_heads / num_kv_heads
+  int head_chunks;    // ceil(group / 16): a wave covers at most 16 q heads
+  int num_blocks, max_blocks_per_seq;
+  int part_tokens;    // partition length in tokens (multiple of block_size)
+  int n_parts;        // partitions per sequence slot in the workspace (1 = single pass)
+  int has_new;
+  float scale_log2;   // softmax_scale * log2(e): scores live in the exp2 domain
+  long long total_units;  // batch * n_parts * num_kv_heads * head_chunks
+};
+
+struct VarlenArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  void* out;
+  int32_t* err_flag;
+  int batch, total_q, total_k, num_heads, num_kv_heads, group;
+  int max_len_q, max_len_k;
+  int q_tiles;        // ceil(max_len_q / rows per workgroup)
+  float scale_log2;
+};
+
+// Launchers return hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.
+hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
+                         hipStream_t stream);
+hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
+int varlen_rows_per_workgroup();
+
+}  // namespace pkv

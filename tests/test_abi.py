@@ -1,0 +1,106 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every
+function include/pkv.h declares, and its host-only checks and launch plan
+behave as documented.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_296_amd as p
+    p._load()
+    return p
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for must in ("pkv_decode", "pkv_varlen", "pkv_decode_workspace_bytes",
+                 "pkv_check_decode_args", "pkv_check_varlen_args", "pkv_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(pkv):
+    lib = ctypes.CDLL(pkv.lib_path)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings(pkv):
+    assert pkv.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert pkv.status_string(s) not in ("ok", "unknown status")
+    assert pkv.status_string(99) == "unknown status"
+    assert pkv.abi_version() >= 1
+
+
+@pytest.mark.parametrize("args,want", [
+    # dtype, has_new, batch, Hq, Hkv, D, num_blocks, bs, max_blocks, partition
+    ((1, 0, 64, 32, 8, 128, 20000, 16, 256, 0), 0),
+    ((0, 1, 3, 4, 4, 64, 8, 32, 4, 0), 0),
+    ((1, 0, 4, 6, 4, 128, 10, 16, 4, 0), 1),      # Hq % Hkv != 0
+    ((1, 0, 4, 8, 4, 96, 10, 16, 4, 0), 2),       # head_dim 96 unsupported
+    ((1, 0, 4, 8, 4, 128, 10, 8, 4, 0), 2),       # block_size 8 unsupported
+    ((2, 0, 4, 8, 4, 128, 10, 16, 4, 0), 2),      # unknown dtype
+    ((1, 0, -1, 8, 4, 128, 10, 16, 4, 0), 1),     # negative batch
+    ((1, 0, 4, 8, 0, 128, 10, 16, 4, 0), 1),      # zero kv heads
+    ((1, 0, 4, 8, 4, 128, 10, 16, 4, 24), 2),     # partition not a block multiple
+    ((1, 0, 4, 8, 4, 128, 10, 16, 4, 16 * 257), 2),  # partition beyond 256 blocks
+    ((1, 2, 4, 8, 4, 128, 10, 16, 4, 0), 1),      # has_new must be 0/1
+])
+def test_check_decode_args(pkv, args, want):
+    assert pkv.check_decode_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((1, 16, 100, 200, 32, 8, 128, 50, 60), 0),
+    ((0, 16, 100, 200, 32, 8, 128, 50, 60), 2),   # fp32 varlen not built
+    ((1, 16, 100, 200, 32, 8, 80, 50, 60), 2),
+    ((1, 16, 100, 200, 30, 8, 128, 50, 60), 1),
+    ((1, -1, 100, 200, 32, 8, 128, 50, 60), 1),
+])
+def test_check_varlen_args(pkv, args, want):
+    assert pkv.check_varlen_args(*args) == want
+
+
+def test_partition_plan_and_workspace(pkv):
+    # explicit partition: 512 tokens over a 2048-block row -> 64 partitions
+    assert pkv.decode_partition_tokens(256, 64, 8, 128, 16, 2048, 512) == 512
+    ws = pkv.decode_workspace_bytes(256, 64, 8, 128, 16, 2048, 512)
+    slots = 256 * 64 * 64
+    assert ws >= slots * (128 + 2) * 4
+    # the tiny example fits one pass: no workspace
+    p = pkv.decode_partition_tokens(3, 4, 4, 64, 32, 4, 0)
+    assert p >= 4 * 32
+    assert pkv.decode_workspace_bytes(3, 4, 4, 64, 32, 4, 0) == 0
+    # library choice is a block multiple within the LDS slice
+    for args in [(64, 32, 8, 128, 16, 256), (512, 32, 8, 128, 16, 513), (1, 8, 1, 128, 32, 4096)]:
+        p = pkv.decode_partition_tokens(*args, 0)
+        assert p > 0 and p % args[4] == 0 and p // args[4] <= 256
+    # rejected arguments give -1 / 0
+    assert pkv.decode_partition_tokens(4, 6, 4, 128, 16, 4, 0) == -1
+    assert pkv.decode_workspace_bytes(4, 6, 4, 128, 16, 4, 0) == 0
+
+
+def test_product_path_refuses_cpu_tensors(pkv):
+    import torch
+    q = torch.zeros(1, 1, 4, 64)
+    kc = torch.zeros(2, 16, 4, 64)
+    bt = torch.zeros(1, 2, dtype=torch.int32)
+    sl = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.decode(q, kc, kc.clone(), bt, sl)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.varlen(torch.zeros(1, 4, 4, 64), torch.zeros(1, 4, 4, 64), torch.zeros(1, 4, 4, 64),
+                   torch.tensor([0, 4], dtype=torch.int32), torch.tensor([0, 4], dtype=torch.int32), 4, 4)

@@ -220,8 +220,9 @@ def make_varlen(*, seed, dtype, batch, num_heads, num_kv_heads, head_dim, q_leng
                       softmax_scale=softmax_scale, q_lengths=lq, k_lengths=lk, seed=seed)
 
 
-def make_config(name: str, device="cpu"):
-    """The named workload: a DecodeCase, a VarlenCase, or (decode, varlen)."""
+def make_config(name: str, device="cpu", part=None):
+    """The named workload: a DecodeCase, a VarlenCase, or for the mixed step
+    (decode, varlen) -- or just one of them with part="decode"/"prefill"."""
     c = dict(CONFIGS[name])
     kind = c.pop("kind")
     if kind == "decode":
@@ -229,9 +230,16 @@ def make_config(name: str, device="cpu"):
     if kind == "varlen":
         return make_varlen(device=device, **c)
     common = {k: c[k] for k in ("dtype", "num_heads", "num_kv_heads", "head_dim")}
-    d = make_decode(device=device, seed=c["seed"], free_list_boundary_alloc=True, **common,
-                    **c["decode"])
-    p = make_varlen(device=device, seed=c["seed"] + 1000, **common, **c["prefill"])
+    d = p = None
+    if part in (None, "decode"):
+        d = make_decode(device=device, seed=c["seed"], free_list_boundary_alloc=True, **common,
+                        **c["decode"])
+    if part in (None, "prefill"):
+        p = make_varlen(device=device, seed=c["seed"] + 1000, **common, **c["prefill"])
+    if part == "decode":
+        return d
+    if part == "prefill":
+        return p
     return d, p
 
 
