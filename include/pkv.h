@@ -88,16 +88,17 @@ int pkv_check_decode_args(int dtype, int has_new, int batch, int num_heads, int 
  * The split-context partition pkv_decode will use for these arguments, in
  * tokens: either the caller's non-zero partition_tokens, or the library's
  * choice for 0.  A result >= max_blocks_per_seq * block_size means a single
- * pass (no partial results, no merge, no workspace).  Returns -1 when
+ * pass (no partial results and no merge).  Returns -1 when
  * pkv_check_decode_args fails.
  */
 int pkv_decode_partition_tokens(int batch, int num_heads, int num_kv_heads, int head_dim,
                                 int block_size, int max_blocks_per_seq, int partition_tokens);
 
 /*
- * Bytes of device workspace pkv_decode needs: fp32 partial results
- * (m, l, acc[head_dim]) for every (sequence, q head, partition).  0 for a
- * single pass.  Returns 0 for arguments pkv_check_decode_args rejects.
+ * Bytes of device workspace pkv_decode needs: a work list of (sequence,
+ * partition) items and a ticket counter, plus, with a split, fp32 partial
+ * results (m, l, acc[head_dim]) for every (sequence, q head, partition).
+ * Returns 0 for arguments pkv_check_decode_args rejects.
  */
 size_t pkv_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, int head_dim,
                                   int block_size, int max_blocks_per_seq, int partition_tokens);
@@ -129,7 +130,8 @@ size_t pkv_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, in
  *                    fixed logical token ranges; their partial (m, l, acc)
  *                    are merged by a second kernel.
  *   workspace      device buffer of at least pkv_decode_workspace_bytes(...)
- *                    bytes (may be NULL when that is 0).  Scratch only.
+ *                    bytes.  Scratch only: its contents need no
+ *                    initialisation and are meaningless after the call.
  *   err_flag       device int32, optional (NULL = no reporting); PKV_ERR_* bits.
  *   stream         hipStream_t.
  *
@@ -145,6 +147,35 @@ int pkv_decode(int dtype, const void* q, void* k_cache, void* v_cache,
                float softmax_scale, int partition_tokens,
                void* workspace, size_t workspace_bytes,
                int32_t* err_flag, void* stream);
+
+/*
+ * The two phases of pkv_decode as separate calls, same arguments and same
+ * checks.  pkv_decode_partials enqueues the per-partition kernel (and the
+ * in-place append): with a split it writes fp32 partial results (m, l,
+ * acc[head_dim]) of every (sequence, q head, partition) into the workspace,
+ * without a split it writes `out` directly.  pkv_decode_merge enqueues the
+ * merge of those partials into `out` (m = max m_k, l = sum l_k e^(m_k - m),
+ * out = sum acc_k e^(m_k - m) / l; inference-notes section 3) and does
+ * nothing without a split.  Calling partials then merge on one stream with
+ * the same arguments and workspace is exactly pkv_decode.  The workspace
+ * layout is private to this library version.
+ */
+int pkv_decode_partials(int dtype, const void* q, void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* cache_seqlens,
+                        const void* k_new, const void* v_new, void* out,
+                        int batch, int num_heads, int num_kv_heads, int head_dim,
+                        int num_blocks, int block_size, int max_blocks_per_seq,
+                        float softmax_scale, int partition_tokens,
+                        void* workspace, size_t workspace_bytes,
+                        int32_t* err_flag, void* stream);
+int pkv_decode_merge(int dtype, const void* q, void* k_cache, void* v_cache,
+                     const int32_t* block_table, const int32_t* cache_seqlens,
+                     const void* k_new, const void* v_new, void* out,
+                     int batch, int num_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int block_size, int max_blocks_per_seq,
+                     float softmax_scale, int partition_tokens,
+                     void* workspace, size_t workspace_bytes,
+                     int32_t* err_flag, void* stream);
 
 /*
  * Host-only validation of pkv_varlen's scalar arguments.  Supported: bf16;

@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = [
-    "PkvError", "decode", "varlen", "decode_workspace_bytes", "decode_partition_tokens",
+    "PkvError", "decode", "decode_partials", "decode_merge", "varlen", "decode_workspace_bytes", "decode_partition_tokens",
     "check_decode_args", "check_varlen_args", "status_string", "abi_version", "lib_path",
     "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
 ]
@@ -56,8 +56,10 @@ def _load():
         L.pkv_decode_partition_tokens.restype = I
         L.pkv_decode_workspace_bytes.argtypes = [I] * 7
         L.pkv_decode_workspace_bytes.restype = SZ
-        L.pkv_decode.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, SZ, P, P]
-        L.pkv_decode.restype = I
+        for name in ("pkv_decode", "pkv_decode_partials", "pkv_decode_merge"):
+            fn = getattr(L, name)
+            fn.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, SZ, P, P]
+            fn.restype = I
         L.pkv_check_varlen_args.argtypes = [I] * 9
         L.pkv_check_varlen_args.restype = I
         L.pkv_varlen.argtypes = [I, P, P, P, P, P, I, I, P, I, I, I, I, I, I, F, P, P]
@@ -138,6 +140,34 @@ def decode(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=No
     append, not modified); k_new/v_new [B, 1, Hkv, D] or None.  Returns out
     [B, 1, Hq, D] in q's dtype.
     """
+    return _decode_call("pkv_decode", q, k_cache, v_cache, block_table, cache_seqlens, k_new,
+                        v_new, softmax_scale, partition_tokens, out, workspace, err_flag,
+                        stream)[0]
+
+
+def decode_partials(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None, *,
+                    softmax_scale=None, partition_tokens=0, out=None, workspace=None,
+                    err_flag=None, stream=None):
+    """First phase of decode (per-partition kernel and the append).  Returns
+    (out, workspace); pass both to decode_merge with the same arguments."""
+    return _decode_call("pkv_decode_partials", q, k_cache, v_cache, block_table, cache_seqlens,
+                        k_new, v_new, softmax_scale, partition_tokens, out, workspace, err_flag,
+                        stream)
+
+
+def decode_merge(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None, *,
+                 softmax_scale=None, partition_tokens=0, out=None, workspace=None, err_flag=None,
+                 stream=None):
+    """Second phase of decode: merge the partials in `workspace` into `out`."""
+    if out is None:
+        raise ValueError("decode_merge needs the out tensor decode_partials returned")
+    return _decode_call("pkv_decode_merge", q, k_cache, v_cache, block_table, cache_seqlens, k_new,
+                        v_new, softmax_scale, partition_tokens, out, workspace, err_flag,
+                        stream)[0]
+
+
+def _decode_call(fname, q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new,
+                 softmax_scale, partition_tokens, out, workspace, err_flag, stream):
     lib = _load()
     _need_gpu(q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new, out, workspace,
               err_flag)
@@ -174,15 +204,17 @@ def decode(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=No
         raise ValueError("out must match q's shape and dtype")
     need = lib.pkv_decode_workspace_bytes(B, Hq, Hkv, D, bs, maxb, int(partition_tokens))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        if fname == "pkv_decode_merge":
+            raise ValueError("decode_merge needs the workspace decode_partials filled")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.pkv_decode(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+    rc = getattr(lib, fname)(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                         _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new), _ptr(out), B, Hq, Hkv, D,
                         NB, bs, maxb, float(softmax_scale), int(partition_tokens),
                         _ptr(workspace), wbytes, _ptr(err_flag), _stream(stream))
     if rc:
-        raise PkvError(rc, "pkv_decode")
-    return out
+        raise PkvError(rc, fname)
+    return out, workspace
 
 
 def varlen(q, k, v, cu_seq_lens_q, cu_seq_lens_k, max_length_q, max_length_k, *,

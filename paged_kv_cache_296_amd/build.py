@@ -21,10 +21,17 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  decode.hip: the atomic optimizer would rewrite the
+# single-lane work-ticket atomic into a wave-wide scan that consumes the
+# returned value at once, stalling on it instead of letting it arrive while
+# the current unit streams.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src):
     obj = os.path.join(CSRC, "_obj", os.path.basename(src) + ".o")
     os.makedirs(os.path.dirname(obj), exist_ok=True)
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

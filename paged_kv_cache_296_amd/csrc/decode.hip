@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "pkv_kernels.h"
 
 namespace pkv {
@@ -49,7 +51,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;        // waves per workgroup (independent units)
+constexpr int kWaves = 2;        // waves per workgroup (independent units)
 constexpr int kMaxSlice = 256;   // table entries one partition may span
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u;
 
@@ -81,25 +83,6 @@ struct Words<false> {
   using word = float;
 };
 
-template <bool BF16, int N>
-__device__ __forceinline__ void load_words(const char* p, typename Words<BF16>::word* w) {
-  using W = Words<BF16>;
-  if constexpr (N == 2) {
-    typename W::vec2 x = *reinterpret_cast<const typename W::vec2*>(p);
-    w[0] = x[0];
-    w[1] = x[1];
-  } else {
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      typename W::vec x = *reinterpret_cast<const typename W::vec*>(p + 16 * i);
-      w[4 * i] = x[0];
-      w[4 * i + 1] = x[1];
-      w[4 * i + 2] = x[2];
-      w[4 * i + 3] = x[3];
-    }
-  }
-}
-
 template <bool BF16, class S>
 struct Tile {
   using W = Words<BF16>;
@@ -122,24 +105,84 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
          ((u32)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
-// Issue the loads of one 16-token tile.  kt/vt point at the tile's first
-// token row of this kv head (uniform); tok is the byte stride between tokens.
-// With new_slot >= 0, the lanes holding that token read k_new/v_new instead
-// of the cache (the cache slot is being written by this call).
-template <bool BF16, class S, bool GENERAL>
-__device__ __forceinline__ void load_tile(Tile<BF16, S>& r, const char* kt, const char* vt, int tok,
-                                          int lane, int new_slot, const char* knew,
-                                          const char* vnew) {
+constexpr int kRsrcFlags = 0x00020000;  // gfx9-family buffer descriptor word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kRsrcFlags);
+}
+
+// V words of one token for this lane: E elements at byte voff + soff.
+template <bool BF16, class S>
+__device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                       typename Words<BF16>::word* w) {
+  using W = Words<BF16>;
+  if constexpr (S::VW == 2) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const typename W::vec2 y = __builtin_bit_cast(typename W::vec2, x);
+    w[0] = y[0];
+    w[1] = y[1];
+  } else {
+#pragma unroll
+    for (int j = 0; j < S::VW / 4; ++j) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * j, soff, 0);
+      const typename W::vec y = __builtin_bit_cast(typename W::vec, x);
+      w[4 * j] = y[0];
+      w[4 * j + 1] = y[1];
+      w[4 * j + 2] = y[2];
+      w[4 * j + 3] = y[3];
+    }
+  }
+}
+
+// Issue the loads of one 16-token tile.  tk/tv point at the tile's first
+// token row of this kv head (uniform, 64-bit scalar); `bytes` is what is left
+// of the physical block from there, so the buffer descriptors bound every
+// access to the block.  koff/voff are the lane's loop-invariant offsets.
+template <bool BF16, class S>
+__device__ __forceinline__ void load_tile(Tile<BF16, S>& r, const char* tk, const char* tv,
+                                          int bytes, int koff, int voff, int tok) {
+  using W = Words<BF16>;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(tk, bytes), rv = rsrc(tv, bytes);
+#pragma unroll
+  for (int t = 0; t < S::NKL; ++t)
+    r.k[t] = __builtin_bit_cast(typename W::vec,
+                                __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * t, 0, 0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_v<BF16, S>(rv, voff, i * tok, r.v[i]);
+}
+
+// A one-token tile holding the new token (token 0; every other slot zero),
+// read from k_new/v_new: the cache slot is being written by this call and is
+// never read back.
+template <bool BF16, class S>
+__device__ __forceinline__ void new_token_tile(Tile<BF16, S>& r, int lane, const char* knew,
+                                               const char* vnew) {
+  using W = Words<BF16>;
   const int r16 = lane & 15, q4 = lane >> 4;
-  const char* kp = kt + r16 * tok + 16 * q4;
-  if (GENERAL && r16 == new_slot) kp = knew + 16 * q4;
+  const typename W::vec z = {0, 0, 0, 0};
 #pragma unroll
-  for (int t = 0; t < S::NKL; ++t) r.k[t] = *reinterpret_cast<const typename Words<BF16>::vec*>(kp + 64 * t);
+  for (int t = 0; t < S::NKL; ++t)
+    r.k[t] = r16 == 0 ? *reinterpret_cast<const typename W::vec*>(knew + 16 * q4 + 64 * t) : z;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const char* vp = vt + (4 * q4 + i) * tok + r16 * (S::E * S::ESZ);
-    if (GENERAL && 4 * q4 + i == new_slot) vp = vnew + r16 * (S::E * S::ESZ);
-    load_words<BF16, S::VW>(vp, r.v[i]);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 0; w < S::VW; ++w) r.v[i][w] = 0;
+  if (q4 == 0) {
+    const char* p = vnew + r16 * (S::E * S::ESZ);
+    if constexpr (S::VW == 2) {
+      const typename W::vec2 x = *reinterpret_cast<const typename W::vec2*>(p);
+      r.v[0][0] = x[0];
+      r.v[0][1] = x[1];
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::VW / 4; ++j) {
+        const typename W::vec x = *reinterpret_cast<const typename W::vec*>(p + 16 * j);
+        r.v[0][4 * j] = x[0];
+        r.v[0][4 * j + 1] = x[1];
+        r.v[0][4 * j + 2] = x[2];
+        r.v[0][4 * j + 3] = x[3];
+      }
+    }
   }
 }
 
@@ -242,23 +285,13 @@ __device__ __forceinline__ void store_out(char* dst, const float* o) {
   }
 }
 
+// One unit of work: (sequence, partition, kv head, chunk of <= 16 q heads).
 template <bool BF16, int D, int BS>
-__global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, int lane, int seq,
+                                            int part, int L, int kvh, int hc) {
   using S = Shape<BF16, D>;
-  __shared__ int slice[kWaves][kMaxSlice];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  long long unit = (long long)blockIdx.x * kWaves + wave;
-  if (unit >= a.total_units) return;
-  const int hc = (int)(unit % a.head_chunks);
-  unit /= a.head_chunks;
-  const int kvh = (int)(unit % a.num_kv_heads);
-  unit /= a.num_kv_heads;
-  const int part = (int)(unit % a.n_parts);
-  const int seq = (int)(unit / a.n_parts);
   const int r16 = lane & 15, q4 = lane >> 4;
 
-  const int L = __builtin_amdgcn_readfirstlane(a.cache_seqlens[seq]);
   const int Lp = L + a.has_new;
   const int tb = part * a.part_tokens;
 
@@ -306,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
   for (int e = lane; e < nblk; e += 64) {
     const int pb = row[e];
     bad |= (pb < 0) | (pb >= a.num_blocks);
-    slice[wave][e] = pb;
+    slice_w[e] = pb;
   }
   if (__any(bad)) {
     fail(kErrBlock);
@@ -326,7 +359,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
   // in-place append of the new token: one wave per (sequence, kv head)
   const bool owns_new = a.has_new && L >= tb && L < te;
   if (owns_new && hc == 0) {
-    const int pb = slice[wave][(L - tb) / BS];
+    const int pb = slice_w[(L - tb) / BS];
     const long long off = (long long)pb * blk + (long long)(L % BS) * tok + (long long)kvh * S::ROW;
     for (int c = lane; c < S::ROW / 16; c += 64) {
       *reinterpret_cast<u32x4*>((char*)a.k_cache + off + 16 * c) =
@@ -353,52 +386,74 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
 #pragma unroll
   for (int c = 0; c < S::NACC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = (te - tb + 15) / 16;
-  auto tile_ptrs = [&](int t, const char*& kt, const char*& vt) {
-    const int pb = __builtin_amdgcn_readfirstlane(slice[wave][(16 * t) / BS]);
-    const long long off = (long long)pb * blk + (long long)((16 * t) % BS) * tok;
-    kt = kbase + off;
-    vt = vbase + off;
+  // cached tokens of this partition are tiled; the new token (if this
+  // partition owns it) is folded in last as its own one-token tile
+  const int tend = owns_new ? L : te;
+  const int ntiles = (tend - tb + 15) / 16;
+  const int last = ntiles - 1;
+  const int nvalid_last = tend - (tb + 16 * last);
+  const int koff = r16 * tok + 16 * q4;
+  const int voff = 4 * q4 * tok + r16 * (S::E * S::ESZ);
+
+  auto issue = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
+    const int pb = __builtin_amdgcn_readfirstlane(slice_w[(16 * t) / BS]);
+    const int inblk = (16 * t) % BS;
+    const long long off = (long long)pb * blk + (long long)inblk * tok;
+    load_tile<BF16, S>(r, kbase + off, vbase + off, (BS - inblk) * tok, koff, voff, tok);
+  };
+  auto compute_full = [&](Tile<BF16, S>& r) __attribute__((always_inline)) {
+    tile_update<BF16, S, false>(r, tile_scores<BF16, S>(r, qr), 16, lane, a.scale_log2, m_run,
+                                l_run, acc);
+  };
+  auto compute = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
+    if (t == last)
+      tile_update<BF16, S, true>(r, tile_scores<BF16, S>(r, qr), nvalid_last, lane, a.scale_log2,
+                                 m_run, l_run, acc);
+    else
+      compute_full(r);
   };
 
-  if (ntiles > 0) {
-    const int last = ntiles - 1;
-    const int last_start = tb + 16 * last;
-    const int nvalid_last = te - last_start;
-    const int new_slot_last = owns_new ? L - last_start : -1;
-    Tile<BF16, S> b0, b1;
-    const char *kt, *vt;
-    tile_ptrs(0, kt, vt);
-    if (last == 0)
-      load_tile<BF16, S, true>(b0, kt, vt, tok, lane, new_slot_last, knew, vnew);
-    else
-      load_tile<BF16, S, false>(b0, kt, vt, tok, lane, -1, nullptr, nullptr);
-    int t = 0;
-    // steady state: two full tiles per trip, the following tile always in flight
-    for (; t + 2 < last; t += 2) {
-      tile_ptrs(t + 1, kt, vt);
-      load_tile<BF16, S, false>(b1, kt, vt, tok, lane, -1, nullptr, nullptr);
-      tile_update<BF16, S, false>(b0, tile_scores<BF16, S>(b0, qr), 16, lane, a.scale_log2, m_run, l_run, acc);
-      tile_ptrs(t + 2, kt, vt);
-      load_tile<BF16, S, false>(b0, kt, vt, tok, lane, -1, nullptr, nullptr);
-      tile_update<BF16, S, false>(b1, tile_scores<BF16, S>(b1, qr), 16, lane, a.scale_log2, m_run, l_run, acc);
+  {
+    // three-tile register ring: while one tile is computed, the next two are
+    // in flight.  The steady-state trip is branch free so the wait counts
+    // stay exact; the last 2..4 tiles are finished after it.
+    Tile<BF16, S> b0, b1, b2;
+    if (ntiles > 0) {
+      // straight-line prologue (a single-tile partition loads its tile
+      // twice): a conditional issue on the way into the loop would make
+      // every wait in it conservative
+      issue(0, b0);
+      issue(min(1, last), b1);
+      int t = 0;
+      // sched_barrier keeps the compiler from hoisting work on a tile whose
+      // loads were just issued above the compute of the tile before it
+      // (that would turn the ring back into a wait for every load in flight)
+      for (; t + 5 <= ntiles; t += 3) {
+        issue(t + 2, b2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(b0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + 3, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(b1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + 4, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(b2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int rem = ntiles - t;  // 1..4 tiles left; t, t+1 already issued
+      if (rem >= 3) issue(t + 2, b2);
+      compute(t, b0);
+      if (rem >= 4) issue(t + 3, b0);
+      if (rem >= 2) compute(t + 1, b1);
+      if (rem >= 3) compute(t + 2, b2);
+      if (rem >= 4) compute(t + 3, b0);
     }
-    // t is loaded in b0; finish t .. last
-    if (t + 1 == last) {
-      tile_ptrs(last, kt, vt);
-      load_tile<BF16, S, true>(b1, kt, vt, tok, lane, new_slot_last, knew, vnew);
-      tile_update<BF16, S, false>(b0, tile_scores<BF16, S>(b0, qr), 16, lane, a.scale_log2, m_run, l_run, acc);
-      tile_update<BF16, S, true>(b1, tile_scores<BF16, S>(b1, qr), nvalid_last, lane, a.scale_log2, m_run, l_run, acc);
-    } else if (t + 2 == last) {
-      tile_ptrs(t + 1, kt, vt);
-      load_tile<BF16, S, false>(b1, kt, vt, tok, lane, -1, nullptr, nullptr);
-      tile_update<BF16, S, false>(b0, tile_scores<BF16, S>(b0, qr), 16, lane, a.scale_log2, m_run, l_run, acc);
-      tile_ptrs(last, kt, vt);
-      load_tile<BF16, S, true>(b0, kt, vt, tok, lane, new_slot_last, knew, vnew);
-      tile_update<BF16, S, false>(b1, tile_scores<BF16, S>(b1, qr), 16, lane, a.scale_log2, m_run, l_run, acc);
-      tile_update<BF16, S, true>(b0, tile_scores<BF16, S>(b0, qr), nvalid_last, lane, a.scale_log2, m_run, l_run, acc);
-    } else {  // t == last (single tile)
-      tile_update<BF16, S, true>(b0, tile_scores<BF16, S>(b0, qr), nvalid_last, lane, a.scale_log2, m_run, l_run, acc);
+    if (owns_new) {
+      new_token_tile<BF16, S>(b1, lane, knew, vnew);
+      tile_update<BF16, S, true>(b1, tile_scores<BF16, S>(b1, qr), 1, lane, a.scale_log2, m_run,
+                                 l_run, acc);
     }
   }
 
@@ -415,6 +470,107 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
   write_result(m_run, l_tot, o);
 }
 
+// Persistent per-partition kernel: each wave takes units by ticket from the
+// work list the plan kernel built (full partitions first, the shorter last
+// partitions after them), prefetching its next ticket while it works, until
+// the list is exhausted.  No workgroup is launched for an empty partition and
+// the tail drains on the shortest units.
+template <bool BF16, int D, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+void decode_partial_kernel(DecodeArgs a) {
+  __shared__ int slice[kWaves][kMaxSlice];
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform; saying so keeps everything derived from it
+  // (unit, kv head, block bases, buffer descriptors) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int per_item = a.num_kv_heads * a.head_chunks;
+  const unsigned total = (unsigned)a.ctrl[1] * (unsigned)per_item;
+  int ticket = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
+  for (;;) {
+    const unsigned u = (unsigned)__builtin_amdgcn_readfirstlane(ticket);
+    if (u >= total) break;
+    ticket = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
+    const int4 item = a.items[u / (unsigned)per_item];
+    const int r = (int)(u % (unsigned)per_item);
+    decode_unit<BF16, D, BS>(a, slice[wave], lane, __builtin_amdgcn_readfirstlane(item.x),
+                             __builtin_amdgcn_readfirstlane(item.y),
+                             __builtin_amdgcn_readfirstlane(item.z), r / a.head_chunks,
+                             r % a.head_chunks);
+  }
+}
+
+// Work list for the persistent kernel, one workgroup: for every sequence its
+// full partitions, then (after all full partitions of all sequences) its
+// last partial one, each item carrying (sequence, partition, cached length); a sequence with nothing to attend or a bad length gets
+// one unit so that its output is written.  Also resets the ticket counter.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int block_size) {
+  __shared__ int s_full[1024], s_part[1024];
+  __shared__ int carry_full, carry_part, total_full;
+  const int tid = threadIdx.x;
+  const long long span = (long long)a.max_blocks_per_seq * block_size;
+  auto counts = [&](int i, int& nf, int& np) {
+    const int L = a.cache_seqlens[i];
+    const int Lp = L + a.has_new;
+    if (L < 0 || (long long)Lp > span) {
+      nf = 0;
+      np = 1;
+      return;
+    }
+    nf = Lp / a.part_tokens;
+    np = (Lp % a.part_tokens != 0 || Lp == 0) ? 1 : 0;
+  };
+  // pass 1: number of full partitions over the batch
+  int my = 0;
+  for (int i = tid; i < a.batch; i += 1024) {
+    int nf, np;
+    counts(i, nf, np);
+    my += nf;
+  }
+  s_full[tid] = my;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) s_full[tid] += s_full[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    total_full = s_full[0];
+    carry_full = 0;
+    carry_part = 0;
+    a.ctrl[0] = 0;
+  }
+  __syncthreads();
+  // pass 2: exclusive scans in chunks of 1024 sequences, then write items
+  for (int base = 0; base < a.batch; base += 1024) {
+    const int i = base + tid;
+    int nf = 0, np = 0;
+    if (i < a.batch) counts(i, nf, np);
+    s_full[tid] = nf;
+    s_part[tid] = np;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int vf = tid >= off ? s_full[tid - off] : 0;
+      const int vp = tid >= off ? s_part[tid - off] : 0;
+      __syncthreads();
+      s_full[tid] += vf;
+      s_part[tid] += vp;
+      __syncthreads();
+    }
+    const int ef = carry_full + s_full[tid] - nf;  // exclusive offsets
+    const int ep = carry_part + s_part[tid] - np;
+    const int L = i < a.batch ? a.cache_seqlens[i] : 0;
+    for (int p = 0; p < nf; ++p) a.items[ef + p] = make_int4(i, p, L, 0);
+    if (np) a.items[total_full + ep] = make_int4(i, nf, L, 0);
+    __syncthreads();
+    if (tid == 1023) {
+      carry_full += s_full[1023];
+      carry_part += s_part[1023];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.ctrl[1] = total_full + carry_part;
+}
+
+
 // Merge of the partitions of one (sequence, q head): m = max m_k,
 // l = sum l_k 2^(m_k - m), out = sum acc_k 2^(m_k - m) / l, in fixed order.
 template <bool BF16, int D, int BS>
@@ -422,7 +578,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   using S = Shape<BF16, D>;
   constexpr int PER = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
-  const long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long idx = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (idx >= (long long)a.batch * a.num_heads) return;
   const int seq = (int)(idx / a.num_heads);
   const int L = __builtin_amdgcn_readfirstlane(a.cache_seqlens[seq]);
@@ -484,16 +640,42 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   store();
 }
 
+// Workgroups of the persistent kernel that fit on the device at once; queried
+// once per device and kernel (launch geometry only, no other state).
+template <class Kernel>
+int resident_workgroups(Kernel kernel, int threads) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  const int v = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 256);
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 template <bool BF16, int D, int BS>
-hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-  const long long wgs = (a.total_units + kWaves - 1) / kWaves;
-  if (wgs > 0) {
-    hipLaunchKernelGGL((decode_partial_kernel<BF16, D, BS>), dim3((unsigned)wgs), dim3(kWaves * 64),
-                       0, stream, a);
+hipError_t launch_one(const DecodeArgs& a, int phases, hipStream_t stream) {
+  if (phases & 1) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a, BS);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const auto kernel = decode_partial_kernel<BF16, D, BS>;
+    long long wgs = resident_workgroups(kernel, kWaves * 64);
+    const long long need = (a.total_units + kWaves - 1) / kWaves;
+    if (wgs > need) wgs = need;
+    if (wgs > 0) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(kWaves * 64), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
-  if (a.n_parts > 1) {
+  if ((phases & 2) && a.n_parts > 1) {
     const long long heads = (long long)a.batch * a.num_heads;
     hipLaunchKernelGGL((decode_merge_kernel<BF16, D, BS>), dim3((unsigned)((heads + 3) / 4)),
                        dim3(256), 0, stream, a);
@@ -505,11 +687,11 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
-                         hipStream_t stream) {
+                         int phases, hipStream_t stream) {
   const bool bf = dtype == 1;
 #define PKV_CASE(B, Dm, BSz)                                           \
   if (bf == B && head_dim == Dm && block_size == BSz)                  \
-    return launch_one<B, Dm, BSz>(a, stream);
+    return launch_one<B, Dm, BSz>(a, phases, stream);
   PKV_CASE(true, 128, 16)
   PKV_CASE(true, 128, 32)
   PKV_CASE(true, 64, 16)

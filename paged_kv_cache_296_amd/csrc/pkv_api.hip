@@ -82,12 +82,27 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int block_siz
   return p;
 }
 
-size_t workspace_for(const DecodePlan& p, int batch, int num_heads, int head_dim) {
-  if (p.n_parts <= 1) return 0;
+// Workspace layout: [ctrl: 256 B][work items: batch * n_parts * 16 B]
+// [partial sums: batch * heads * n_parts * head_dim * 4 B][(m, l) pairs], each
+// part 256-byte aligned.
+struct WorkspaceLayout {
+  size_t items, acc, ml, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WorkspaceLayout layout_for(const DecodePlan& p, int batch, int num_heads, int head_dim) {
+  WorkspaceLayout w;
   const size_t slots = (size_t)batch * num_heads * p.n_parts;
-  size_t acc = slots * head_dim * sizeof(float);
-  acc = (acc + 255) & ~(size_t)255;
-  return acc + slots * 2 * sizeof(float);
+  w.items = 256;
+  w.acc = w.items + align256((size_t)batch * p.n_parts * 16);
+  w.ml = w.acc + (p.n_parts > 1 ? align256(slots * head_dim * sizeof(float)) : 0);
+  w.total = w.ml + (p.n_parts > 1 ? align256(slots * 2 * sizeof(float)) : 0);
+  return w;
+}
+
+size_t workspace_for(const DecodePlan& p, int batch, int num_heads, int head_dim) {
+  return layout_for(p, batch, num_heads, head_dim).total;
 }
 
 }  // namespace
@@ -134,14 +149,18 @@ size_t pkv_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, in
   return workspace_for(p, batch, num_heads, head_dim);
 }
 
-int pkv_decode(int dtype, const void* q, void* k_cache, void* v_cache,
-               const int32_t* block_table, const int32_t* cache_seqlens,
-               const void* k_new, const void* v_new, void* out,
-               int batch, int num_heads, int num_kv_heads, int head_dim,
-               int num_blocks, int block_size, int max_blocks_per_seq,
-               float softmax_scale, int partition_tokens,
-               void* workspace, size_t workspace_bytes,
-               int32_t* err_flag, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(int phases, int dtype, const void* q, void* k_cache, void* v_cache,
+                const int32_t* block_table, const int32_t* cache_seqlens,
+                const void* k_new, const void* v_new, void* out,
+                int batch, int num_heads, int num_kv_heads, int head_dim,
+                int num_blocks, int block_size, int max_blocks_per_seq,
+                float softmax_scale, int partition_tokens,
+                void* workspace, size_t workspace_bytes,
+                int32_t* err_flag, void* stream) {
   const int has_new = k_new != nullptr;
   if ((k_new == nullptr) != (v_new == nullptr)) return PKV_EINVAL;
   int rc = check_decode(dtype, has_new, batch, num_heads, num_kv_heads, head_dim, num_blocks,
@@ -164,10 +183,11 @@ int pkv_decode(int dtype, const void* q, void* k_cache, void* v_cache,
   a.k_new = k_new;
   a.v_new = v_new;
   a.out = out;
-  const size_t slots = (size_t)batch * num_heads * p.n_parts;
-  a.ws_acc = need ? (float*)workspace : nullptr;
-  size_t acc_bytes = (slots * head_dim * sizeof(float) + 255) & ~(size_t)255;
-  a.ws_ml = need ? (float2*)((char*)workspace + acc_bytes) : nullptr;
+  const WorkspaceLayout wl = layout_for(p, batch, num_heads, head_dim);
+  a.ctrl = (int*)workspace;
+  a.items = (int4*)((char*)workspace + wl.items);
+  a.ws_acc = p.n_parts > 1 ? (float*)((char*)workspace + wl.acc) : nullptr;
+  a.ws_ml = p.n_parts > 1 ? (float2*)((char*)workspace + wl.ml) : nullptr;
   a.err_flag = err_flag;
   a.batch = batch;
   a.num_heads = num_heads;
@@ -182,9 +202,28 @@ int pkv_decode(int dtype, const void* q, void* k_cache, void* v_cache,
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.total_units = (long long)batch * p.n_parts * num_kv_heads * p.head_chunks;
   if (a.total_units >= (1LL << 31)) return PKV_EUNSUPPORTED;
-  hipError_t e = pkv::launch_decode(dtype, head_dim, block_size, a, (hipStream_t)stream);
+  hipError_t e = pkv::launch_decode(dtype, head_dim, block_size, a, phases, (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
+
+}  // namespace
+
+extern "C" {
+
+#define PKV_DECODE_ARGS                                                                        \
+  int dtype, const void *q, void *k_cache, void *v_cache, const int32_t *block_table,          \
+      const int32_t *cache_seqlens, const void *k_new, const void *v_new, void *out,           \
+      int batch, int num_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size, \
+      int max_blocks_per_seq, float softmax_scale, int partition_tokens, void *workspace,      \
+      size_t workspace_bytes, int32_t *err_flag, void *stream
+#define PKV_DECODE_FWD                                                                     \
+  dtype, q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new, out, batch,        \
+      num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,       \
+      softmax_scale, partition_tokens, workspace, workspace_bytes, err_flag, stream
+
+int pkv_decode(PKV_DECODE_ARGS) { return decode_impl(3, PKV_DECODE_FWD); }
+int pkv_decode_partials(PKV_DECODE_ARGS) { return decode_impl(1, PKV_DECODE_FWD); }
+int pkv_decode_merge(PKV_DECODE_ARGS) { return decode_impl(2, PKV_DECODE_FWD); }
 
 int pkv_check_varlen_args(int dtype, int batch, int total_q, int total_k, int num_heads,
                           int num_kv_heads, int head_dim, int max_length_q, int max_length_k) {

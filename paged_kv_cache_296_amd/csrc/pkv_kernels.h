@@ -18,6 +18,8 @@ struct DecodeArgs {
   void* out;
   float* ws_acc;      // [batch, num_heads, n_parts, head_dim] unnormalised sums
   float2* ws_ml;      // [batch, num_heads, n_parts] (running max, sum of exponentials)
+  int* ctrl;          // [0] ticket counter, [1] number of work items (written by the plan kernel)
+  int4* items;        // [batch * n_parts] work items (sequence, partition, cached length, 0)
   int32_t* err_flag;  // may be null
   int batch, num_heads, num_kv_heads, group;  // group = num_heads / num_kv_heads
   int head_chunks;    // ceil(group / 16): a wave covers at most 16 q heads
@@ -26,7 +28,7 @@ struct DecodeArgs {
   int n_parts;        // partitions per sequence slot in the workspace (1 = single pass)
   int has_new;
   float scale_log2;   // softmax_scale * log2(e): scores live in the exp2 domain
-  long long total_units;  // batch * n_parts * num_kv_heads * head_chunks
+  long long total_units;  // upper bound: batch * n_parts * num_kv_heads * head_chunks
 };
 
 struct VarlenArgs {
@@ -44,8 +46,9 @@ struct VarlenArgs {
 };
 
 // Launchers return hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.
+// phases: bit 0 = per-partition kernel (with the append), bit 1 = merge.
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
-                         hipStream_t stream);
+                         int phases, hipStream_t stream);
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
 int varlen_rows_per_workgroup();
 

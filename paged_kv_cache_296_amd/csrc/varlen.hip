@@ -143,7 +143,8 @@ __global__ __launch_bounds__(256) void varlen_kernel(VarlenArgs a) {
   constexpr int KS = D / 16;     // QK k-steps of 16 dims
   constexpr int DT = D / 32;     // O^T dim tiles
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps row math scalar
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n = lane & 31, hh = lane >> 5;
 

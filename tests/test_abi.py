@@ -80,10 +80,10 @@ def test_partition_plan_and_workspace(pkv):
     ws = pkv.decode_workspace_bytes(256, 64, 8, 128, 16, 2048, 512)
     slots = 256 * 64 * 64
     assert ws >= slots * (128 + 2) * 4
-    # the tiny example fits one pass: no workspace
+    # the tiny example fits one pass: only the work list, no partial results
     p = pkv.decode_partition_tokens(3, 4, 4, 64, 32, 4, 0)
     assert p >= 4 * 32
-    assert pkv.decode_workspace_bytes(3, 4, 4, 64, 32, 4, 0) == 0
+    assert 0 < pkv.decode_workspace_bytes(3, 4, 4, 64, 32, 4, 0) <= 4096
     # library choice is a block multiple within the LDS slice
     for args in [(64, 32, 8, 128, 16, 256), (512, 32, 8, 128, 16, 513), (1, 8, 1, 128, 32, 4096)]:
         p = pkv.decode_partition_tokens(*args, 0)

@@ -271,3 +271,19 @@ def test_empty_batch_and_zero_lengths():
     q0 = case.q[:0]
     out0 = pkv.decode(q0, case.k_cache, case.v_cache, case.block_table[:0], case.cache_seqlens[:0])
     assert out0.shape[0] == 0
+
+
+def test_two_phase_calls_equal_decode_bitwise():
+    case = workloads.make_decode(seed=7300, dtype="bf16", batch=12, num_heads=32, num_kv_heads=8,
+                                 head_dim=128, block_size=16, lengths=("uniform", 1, 2000),
+                                 num_blocks=2000, append=True, partition_tokens=256, device=DEV)
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    ref = pkv.decode(case.q, kc, vc, case.block_table, case.cache_seqlens, case.k_new, case.v_new,
+                     partition_tokens=256)
+    out, ws = pkv.decode_partials(case.q, case.k_cache, case.v_cache, case.block_table,
+                                  case.cache_seqlens, case.k_new, case.v_new, partition_tokens=256)
+    out = pkv.decode_merge(case.q, case.k_cache, case.v_cache, case.block_table,
+                           case.cache_seqlens, case.k_new, case.v_new, partition_tokens=256,
+                           out=out, workspace=ws)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(kc.view(torch.int16), case.k_cache.view(torch.int16))

@@ -136,7 +136,7 @@ class VarlenCase:
 def make_decode(*, seed, dtype, batch, num_heads, num_kv_heads, head_dim, block_size, lengths,
                 num_blocks, max_blocks_per_seq=None, append=False, partition_tokens=0,
                 table=None, free_list_boundary_alloc=False, device="cpu", softmax_scale=None,
-                **_):
+                placement="permuted", **_):
     """A paged decode batch.
 
     With ``append`` the table also holds the block that receives the new
@@ -160,6 +160,8 @@ def make_decode(*, seed, dtype, batch, num_heads, num_kv_heads, head_dim, block_
         bt = np.asarray(table, dtype=np.int32)
     else:
         perm = rng.permutation(num_blocks).astype(np.int32)
+        if placement == "contiguous":      # same draws, blocks handed out in order
+            perm = np.arange(num_blocks, dtype=np.int32)
         if int(need.sum()) > num_blocks:
             raise ValueError("pool too small for the drawn lengths")
         bt = np.full((batch, max_blocks_per_seq), -1, dtype=np.int32)
