@@ -285,32 +285,46 @@ __device__ __forceinline__ void store_out(char* dst, const float* o) {
   }
 }
 
-// One unit of work: (sequence, partition, kv head, chunk of <= 16 q heads).
+// One unit of work: a run of `nparts` consecutive partitions of one
+// sequence, starting at partition `p0`, for one kv head and one chunk of <= 16
+// of its q heads.  The run is streamed as one tile sequence (the register ring
+// never drains inside it).  Each partition starts from a fresh (m, l, acc);
+// at its end the partial is folded into the run's state in LDS with the
+// (m, l) merge, and the run's merged partial is written once, at the end, to
+// the slot of its first partition.  (A global store in mid-stream would make
+// every later tile wait also wait for the store's acknowledgement: the
+// vector-memory counter retires loads and stores in order.)
 template <bool BF16, int D, int BS>
-__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, int lane, int seq,
-                                            int part, int L, int kvh, int hc) {
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, float* run_w,
+                                            int lane, int seq, int p0, int nparts, int L, int kvh,
+                                            int hc) {
   using S = Shape<BF16, D>;
   const int r16 = lane & 15, q4 = lane >> 4;
-
+  const int P = a.part_tokens;
   const int Lp = L + a.has_new;
-  const int tb = part * a.part_tokens;
+  const int tb = p0 * P;
 
   // q head held by this lane (padding lanes: hq < 0)
   const int hin = hc * 16 + r16;
   const int hq = hin < a.group ? kvh * a.group + hin : -1;
   const bool split = a.n_parts > 1;
 
-  auto write_result = [&](float m, float l, const float* o /*4E values*/) {
+  // Partials of one (sequence, kv head, partition) are one block of
+  // group * D floats; this chunk's heads occupy [16 hc D, (16 hc + gc) D) of
+  // it, laid out as [j][q4][head][4] so that each store instruction writes one
+  // contiguous run of 64 gc bytes (not 16-byte pieces a cache line apart).
+  const int gc = min(16, a.group - 16 * hc);
+  auto write_result = [&](int part, float m, float l, const float* o /*4E values*/) {
     if (hq < 0) return;
     if (split) {
-      const long long slot = ((long long)seq * a.num_heads + hq) * a.n_parts + part;
-      float* dst = a.ws_acc + slot * D + 4 * S::E * q4;
+      const long long blk_id = ((long long)seq * a.num_kv_heads + kvh) * a.n_parts + part;
+      float* dst = a.ws_acc + blk_id * a.group * D + 16 * hc * D;
 #pragma unroll
       for (int j = 0; j < S::E; ++j) {
         f32x4 w = {o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-        *reinterpret_cast<f32x4*>(dst + 4 * j) = w;
+        *reinterpret_cast<f32x4*>(dst + 4 * ((j * 4 + q4) * gc + r16)) = w;
       }
-      if (q4 == 0) a.ws_ml[slot] = make_float2(m, l);
+      if (q4 == 0) a.ws_ml[blk_id * a.group + 16 * hc + r16] = make_float2(m, l);
     } else {
       char* dst = (char*)a.out + (((long long)seq * a.num_heads + hq) * D + 4 * S::E * q4) * S::ESZ;
       store_out<BF16, S>(dst, o);
@@ -321,19 +335,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, i
     float o[4 * S::E];
 #pragma unroll
     for (int j = 0; j < 4 * S::E; ++j) o[j] = __builtin_nanf("");
-    write_result(__builtin_nanf(""), __builtin_nanf(""), o);
+    write_result(p0, __builtin_nanf(""), __builtin_nanf(""), o);
   };
 
   if (L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS) {
-    if (part == 0) fail(kErrSpan);
+    fail(kErrSpan);
     return;
   }
-  if (tb >= Lp && part > 0) return;  // partition past the end of this sequence
-  const int te = min(tb + a.part_tokens, Lp);
+  const int te = min(tb + nparts * P, Lp);
   const int nblk = te > tb ? (te - tb + BS - 1) / BS : 0;
   const int jb0 = tb / BS;
 
-  // stage and validate the table slice
+  // stage and validate the table slice of the run
   bool bad = false;
   const int32_t* row = a.block_table + (long long)seq * a.max_blocks_per_seq + jb0;
   for (int e = lane; e < nblk; e += 64) {
@@ -386,12 +399,86 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, i
 #pragma unroll
   for (int c = 0; c < S::NACC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // cached tokens of this partition are tiled; the new token (if this
-  // partition owns it) is folded in last as its own one-token tile
+  // End of partition `part`: fold its (m, l, acc) into the run state, then
+  // start the next partition afresh.  The run state lives in LDS, lane-major
+  // ([value][lane]); the last partition of the run writes the merged partial
+  // (or, without a split, the normalised output).  Values are handled E at a
+  // time (one row i of the accumulators: dims E (4 q4 + i) + c) to keep the
+  // register footprint small.
+  auto flush = [&](int part) __attribute__((always_inline)) {
+    float l_tot = l_run + swap16(l_run);  // total of the 4 token groups of this head
+    l_tot += swap32(l_tot);
+    const bool first = part == p0, final = part == p0 + nparts - 1;
+    float m = m_run, l = l_tot, fa = 0.f, fb = 1.f;
+    if (!first) {
+      // merge with the run so far: m' = max(M, m), l' = L 2^(M-m') + l 2^(m-m')
+      const float M = run_w[4 * S::E * 64 + lane], Lr = run_w[(4 * S::E + 1) * 64 + lane];
+      const float mn = fmaxf(M, m);
+      fa = fast_exp2(M - mn);
+      fb = fast_exp2(m - mn);
+      l = Lr * fa + l * fb;
+      m = mn;
+    }
+    const float inv = (final && !split) ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
+    const long long blk_id = ((long long)seq * a.num_kv_heads + kvh) * a.n_parts + p0;
+    float* wsd = split ? a.ws_acc + blk_id * a.group * D + 16 * hc * D : nullptr;
+    char* outd = (char*)a.out + (((long long)seq * a.num_heads + (hq < 0 ? 0 : hq)) * D +
+                                 4 * S::E * q4) * S::ESZ;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[S::E];
+#pragma unroll
+      for (int c = 0; c < S::E; ++c) {
+        const int j = S::E * i + c;
+        v[c] = first ? acc[c][i] : run_w[j * 64 + lane] * fa + acc[c][i] * fb;
+      }
+      if (!final) {
+#pragma unroll
+        for (int c = 0; c < S::E; ++c) run_w[(S::E * i + c) * 64 + lane] = v[c];
+      } else if (hq >= 0) {
+        if (split) {
+#pragma unroll
+          for (int c = 0; c < S::E; c += 4) {
+            const int j4 = (S::E * i + c) / 4;
+            *reinterpret_cast<f32x4*>(wsd + 4 * ((j4 * 4 + q4) * gc + r16)) =
+                f32x4{v[c], v[c + 1], v[c + 2], v[c + 3]};
+          }
+        } else if constexpr (BF16) {
+          if constexpr (S::E == 8) {
+            *reinterpret_cast<u32x4*>(outd + 16 * i) =
+                u32x4{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv),
+                      pack_bf16x2(v[4] * inv, v[5] * inv), pack_bf16x2(v[6] * inv, v[7] * inv)};
+          } else {
+            *reinterpret_cast<u32x2*>(outd + 8 * i) =
+                u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < S::E; c += 4)
+            *reinterpret_cast<f32x4*>(outd + 4 * (S::E * i + c)) =
+                f32x4{v[c] * inv, v[c + 1] * inv, v[c + 2] * inv, v[c + 3] * inv};
+        }
+      }
+    }
+    if (!final) {
+      run_w[4 * S::E * 64 + lane] = m;
+      run_w[(4 * S::E + 1) * 64 + lane] = l;
+    } else if (split && hq >= 0 && q4 == 0) {
+      a.ws_ml[blk_id * a.group + 16 * hc + r16] = make_float2(m, l);
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int c = 0; c < S::NACC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // cached tokens of the run are tiled; the new token (if the run owns it)
+  // is folded in last as its own one-token tile
   const int tend = owns_new ? L : te;
   const int ntiles = (tend - tb + 15) / 16;
   const int last = ntiles - 1;
   const int nvalid_last = tend - (tb + 16 * last);
+  const int tpp = P / 16;  // tiles per partition (P is a multiple of 16)
   const int koff = r16 * tok + 16 * q4;
   const int voff = 4 * q4 * tok + r16 * (S::E * S::ESZ);
 
@@ -401,27 +488,34 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, i
     const long long off = (long long)pb * blk + (long long)inblk * tok;
     load_tile<BF16, S>(r, kbase + off, vbase + off, (BS - inblk) * tok, koff, voff, tok);
   };
-  auto compute_full = [&](Tile<BF16, S>& r) __attribute__((always_inline)) {
+  // a partition ends after tile t: write its partial (the run's last
+  // partition is written after the loop)
+  auto boundary = [&](int t) __attribute__((always_inline)) {
+    if ((t + 1) % tpp == 0 && t != last) flush(p0 + t / tpp);
+  };
+  auto compute_full = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
     tile_update<BF16, S, false>(r, tile_scores<BF16, S>(r, qr), 16, lane, a.scale_log2, m_run,
                                 l_run, acc);
+    boundary(t);
   };
   auto compute = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
     if (t == last)
       tile_update<BF16, S, true>(r, tile_scores<BF16, S>(r, qr), nvalid_last, lane, a.scale_log2,
                                  m_run, l_run, acc);
     else
-      compute_full(r);
+      compute_full(t, r);
   };
 
   {
     // three-tile register ring: while one tile is computed, the next two are
-    // in flight.  The steady-state trip is branch free so the wait counts
-    // stay exact; the last 2..4 tiles are finished after it.
+    // in flight.  The steady-state trip is branch free except for the rare
+    // partition end, so the wait counts stay tight; the last 1..4 tiles are
+    // finished after it.
     Tile<BF16, S> b0, b1, b2;
     if (ntiles > 0) {
-      // straight-line prologue (a single-tile partition loads its tile
-      // twice): a conditional issue on the way into the loop would make
-      // every wait in it conservative
+      // straight-line prologue (a single-tile run loads its tile twice): a
+      // conditional issue on the way into the loop would make every wait in
+      // it conservative
       issue(0, b0);
       issue(min(1, last), b1);
       int t = 0;
@@ -431,15 +525,15 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, i
       for (; t + 5 <= ntiles; t += 3) {
         issue(t + 2, b2);
         __builtin_amdgcn_sched_barrier(0);
-        compute_full(b0);
+        compute_full(t, b0);
         __builtin_amdgcn_sched_barrier(0);
         issue(t + 3, b0);
         __builtin_amdgcn_sched_barrier(0);
-        compute_full(b1);
+        compute_full(t + 1, b1);
         __builtin_amdgcn_sched_barrier(0);
         issue(t + 4, b1);
         __builtin_amdgcn_sched_barrier(0);
-        compute_full(b2);
+        compute_full(t + 2, b2);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int rem = ntiles - t;  // 1..4 tiles left; t, t+1 already issued
@@ -449,6 +543,9 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, i
       if (rem >= 2) compute(t + 1, b1);
       if (rem >= 3) compute(t + 2, b2);
       if (rem >= 4) compute(t + 3, b0);
+      // a new token that starts a partition of its own: close the last
+      // partition of cached tokens first
+      if (owns_new && L % P == 0) flush(L / P - 1);
     }
     if (owns_new) {
       new_token_tile<BF16, S>(b1, lane, knew, vnew);
@@ -456,29 +553,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, i
                                  l_run, acc);
     }
   }
-
-  // total of the 4 token groups of this head
-  float l_tot = l_run + swap16(l_run);
-  l_tot += swap32(l_tot);
-
-  float o[4 * S::E];
-  const float inv = split ? 1.f : (l_tot > 0.f ? 1.f / l_tot : 0.f);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < S::E; ++c) o[S::E * i + c] = acc[c][i] * inv;
-  write_result(m_run, l_tot, o);
+  flush(p0 + nparts - 1);
 }
 
 // Persistent per-partition kernel: each wave takes units by ticket from the
-// work list the plan kernel built (full partitions first, the shorter last
-// partitions after them), prefetching its next ticket while it works, until
-// the list is exhausted.  No workgroup is launched for an empty partition and
-// the tail drains on the shortest units.
+// work list the plan kernel built, prefetching its next ticket while it
+// works, until the list is exhausted.  No workgroup is launched for an empty
+// partition and the tail drains on the shortest units.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
 void decode_partial_kernel(DecodeArgs a) {
   __shared__ int slice[kWaves][kMaxSlice];
+  __shared__ float run_state[kWaves][(D / 4 + 2) * 64];  // per lane: D/4 sums, m, l
   const int lane = threadIdx.x & 63;
   // the wave index is uniform; saying so keeps everything derived from it
   // (unit, kv head, block bases, buffer descriptors) in scalar registers
@@ -492,152 +578,206 @@ void decode_partial_kernel(DecodeArgs a) {
     ticket = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
     const int4 item = a.items[u / (unsigned)per_item];
     const int r = (int)(u % (unsigned)per_item);
-    decode_unit<BF16, D, BS>(a, slice[wave], lane, __builtin_amdgcn_readfirstlane(item.x),
-                             __builtin_amdgcn_readfirstlane(item.y),
-                             __builtin_amdgcn_readfirstlane(item.z), r / a.head_chunks,
-                             r % a.head_chunks);
+    const int packed = __builtin_amdgcn_readfirstlane(item.y);
+    decode_unit<BF16, D, BS>(a, slice[wave], run_state[wave], lane,
+                             __builtin_amdgcn_readfirstlane(item.x),
+                             packed >> 8, packed & 255, __builtin_amdgcn_readfirstlane(item.z),
+                             r / a.head_chunks, r % a.head_chunks);
   }
 }
 
-// Work list for the persistent kernel, one workgroup: for every sequence its
-// full partitions, then (after all full partitions of all sequences) its
-// last partial one, each item carrying (sequence, partition, cached length); a sequence with nothing to attend or a bad length gets
-// one unit so that its output is written.  Also resets the ticket counter.
+// Direct grid for small batches: one wave per (sequence, partition, kv head,
+// head chunk) slot of the full grid, no work list; slots past a sequence's
+// end exit at once.  For few units the persistent kernel's per-unit work-list
+// lookups would not be hidden.
+template <bool BF16, int D, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+void decode_direct_kernel(DecodeArgs a) {
+  __shared__ int slice[kWaves][kMaxSlice];
+  __shared__ float run_state[kWaves][(D / 4 + 2) * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned unit = blockIdx.x * kWaves + wave;
+  if (unit >= (unsigned)a.total_units) return;
+  const int hc = (int)(unit % (unsigned)a.head_chunks);
+  unit /= (unsigned)a.head_chunks;
+  const int kvh = (int)(unit % (unsigned)a.num_kv_heads);
+  unit /= (unsigned)a.num_kv_heads;
+  const int part = (int)(unit % (unsigned)a.n_parts);
+  const int seq = (int)(unit / (unsigned)a.n_parts);
+  const int L = __builtin_amdgcn_readfirstlane(a.cache_seqlens[seq]);
+  const int Lp = L + a.has_new;
+  const bool bad = L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS;
+  if (part > 0 && (bad || part * a.part_tokens >= Lp)) return;
+  decode_unit<BF16, D, BS>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh, hc);
+}
+
+// Work list for the persistent kernel, one workgroup.  Every sequence's
+// partitions are cut into runs of R consecutive partitions (R chosen so that
+// there are at least about four units per resident wave, and at most
+// a.max_run); full runs of all sequences come first, then each sequence's
+// shorter last run.  A sequence with nothing to attend or a bad length gets
+// one one-partition run so that its output is written.  Items carry
+// (sequence, first partition << 8 | partitions, cached length).  Also resets
+// the ticket counter and records the run length for the merge.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int block_size) {
-  __shared__ int s_full[1024], s_part[1024];
-  __shared__ int carry_full, carry_part, total_full;
+  __shared__ int s_a[1024], s_b[1024];
+  __shared__ int carry_a, carry_b, total_a, run;
   const int tid = threadIdx.x;
   const long long span = (long long)a.max_blocks_per_seq * block_size;
-  auto counts = [&](int i, int& nf, int& np) {
-    const int L = a.cache_seqlens[i];
+  auto nparts_of = [&](int i, int& L) {
+    L = a.cache_seqlens[i];
     const int Lp = L + a.has_new;
-    if (L < 0 || (long long)Lp > span) {
-      nf = 0;
-      np = 1;
-      return;
-    }
-    nf = Lp / a.part_tokens;
-    np = (Lp % a.part_tokens != 0 || Lp == 0) ? 1 : 0;
+    if (L < 0 || (long long)Lp > span || Lp == 0) return 1;
+    return (Lp + a.part_tokens - 1) / a.part_tokens;
   };
-  // pass 1: number of full partitions over the batch
+  auto block_sum = [&](int v) {
+    s_a[tid] = v;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+      if (tid < off) s_a[tid] += s_a[tid + off];
+      __syncthreads();
+    }
+    const int r = s_a[0];
+    __syncthreads();
+    return r;
+  };
+  // pass 1: partitions over the batch -> run length
   int my = 0;
   for (int i = tid; i < a.batch; i += 1024) {
-    int nf, np;
-    counts(i, nf, np);
-    my += nf;
+    int L;
+    my += nparts_of(i, L);
   }
-  s_full[tid] = my;
-  __syncthreads();
-  for (int off = 512; off > 0; off >>= 1) {
-    if (tid < off) s_full[tid] += s_full[tid + off];
-    __syncthreads();
-  }
+  const long long units = (long long)block_sum(my) * a.num_kv_heads * a.head_chunks;
   if (tid == 0) {
-    total_full = s_full[0];
-    carry_full = 0;
-    carry_part = 0;
+    long long r = units / (4LL * a.resident_waves);
+    run = (int)(r < 1 ? 1 : (r > a.max_run ? a.max_run : r));
+  }
+  __syncthreads();
+  const int R = run;
+  // pass 2: number of full runs over the batch
+  my = 0;
+  for (int i = tid; i < a.batch; i += 1024) {
+    int L;
+    my += nparts_of(i, L) / R;
+  }
+  const int full_total = block_sum(my);
+  if (tid == 0) {
+    total_a = full_total;
+    carry_a = 0;
+    carry_b = 0;
     a.ctrl[0] = 0;
   }
   __syncthreads();
-  // pass 2: exclusive scans in chunks of 1024 sequences, then write items
+  // pass 3: exclusive scans in chunks of 1024 sequences, then write items
   for (int base = 0; base < a.batch; base += 1024) {
     const int i = base + tid;
-    int nf = 0, np = 0;
-    if (i < a.batch) counts(i, nf, np);
-    s_full[tid] = nf;
-    s_part[tid] = np;
+    int L = 0, np = 0;
+    if (i < a.batch) np = nparts_of(i, L);
+    const int nf = np / R, nr = (np % R) ? 1 : 0;
+    s_a[tid] = nf;
+    s_b[tid] = nr;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-      const int vf = tid >= off ? s_full[tid - off] : 0;
-      const int vp = tid >= off ? s_part[tid - off] : 0;
+      const int va = tid >= off ? s_a[tid - off] : 0;
+      const int vb = tid >= off ? s_b[tid - off] : 0;
       __syncthreads();
-      s_full[tid] += vf;
-      s_part[tid] += vp;
+      s_a[tid] += va;
+      s_b[tid] += vb;
       __syncthreads();
     }
-    const int ef = carry_full + s_full[tid] - nf;  // exclusive offsets
-    const int ep = carry_part + s_part[tid] - np;
-    const int L = i < a.batch ? a.cache_seqlens[i] : 0;
-    for (int p = 0; p < nf; ++p) a.items[ef + p] = make_int4(i, p, L, 0);
-    if (np) a.items[total_full + ep] = make_int4(i, nf, L, 0);
+    const int ea = carry_a + s_a[tid] - nf;  // exclusive offsets
+    const int eb = carry_b + s_b[tid] - nr;
+    for (int k = 0; k < nf; ++k) a.items[ea + k] = make_int4(i, ((k * R) << 8) | R, L, 0);
+    if (nr) a.items[total_a + eb] = make_int4(i, ((nf * R) << 8) | (np % R), L, 0);
     __syncthreads();
     if (tid == 1023) {
-      carry_full += s_full[1023];
-      carry_part += s_part[1023];
+      carry_a += s_a[1023];
+      carry_b += s_b[1023];
     }
     __syncthreads();
   }
-  if (tid == 0) a.ctrl[1] = total_full + carry_part;
+  if (tid == 0) {
+    a.ctrl[1] = total_a + carry_b;
+    a.ctrl[2] = R;
+  }
 }
 
-
-// Merge of the partitions of one (sequence, q head): m = max m_k,
-// l = sum l_k 2^(m_k - m), out = sum acc_k 2^(m_k - m) / l, in fixed order.
+// Merge of the partials of one (sequence, kv head, chunk of <= 16 q heads),
+// one per run of partitions, one wave: each lane holds the same (q head, D/4
+// dims) it held in the per-partition kernel, so the partials are read back as
+// the contiguous runs they were written as.  m = max m_k,
+// l = sum l_k 2^(m_k - m), sums likewise (in run order), out = sum / l (0 for
+// l = 0); a NaN partial (a data error) makes the output NaN.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   using S = Shape<BF16, D>;
-  constexpr int PER = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
-  const long long idx = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (idx >= (long long)a.batch * a.num_heads) return;
-  const int seq = (int)(idx / a.num_heads);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long gid = (long long)blockIdx.x * 4 + wave;
+  const long long ngroups = (long long)a.batch * a.num_kv_heads * a.head_chunks;
+  if (gid >= ngroups) return;
+  const int hc = (int)(gid % a.head_chunks);
+  const long long sk = gid / a.head_chunks;  // seq * num_kv_heads + kvh
+  const int kvh = (int)(sk % a.num_kv_heads);
+  const int seq = (int)(sk / a.num_kv_heads);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int gc = min(16, a.group - 16 * hc);
+  if (r16 >= gc) return;
+  const int hq = kvh * a.group + 16 * hc + r16;
+  char* dst = (char*)a.out + (((long long)seq * a.num_heads + hq) * D + 4 * S::E * q4) * S::ESZ;
+  float o[4 * S::E];
+
   const int L = __builtin_amdgcn_readfirstlane(a.cache_seqlens[seq]);
   const int Lp = L + a.has_new;
-  char* dst = (char*)a.out + (idx * D + PER * lane) * S::ESZ;
-  float o[PER];
-  auto store = [&]() {
-    if constexpr (BF16) {
-      if constexpr (PER == 2) {
-        *reinterpret_cast<u32*>(dst) = pack_bf16x2(o[0], o[1]);
-      } else {
-        __bf16 h = (__bf16)o[0];
-        *reinterpret_cast<__bf16*>(dst) = h;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) reinterpret_cast<float*>(dst)[j] = o[j];
-    }
-  };
   if (L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) o[j] = __builtin_nanf("");
-    store();
+    for (int j = 0; j < 4 * S::E; ++j) o[j] = __builtin_nanf("");
+    store_out<BF16, S>(dst, o);
     return;
   }
   const int np = Lp > 0 ? (Lp + a.part_tokens - 1) / a.part_tokens : 1;
-  const float2* ml = a.ws_ml + idx * a.n_parts;
-  const float* acc = a.ws_acc + idx * a.n_parts * D + PER * lane;
+  // each run of R partitions left one partial, at its first slot
+  const int R = a.direct ? 1 : a.ctrl[2];
+  const long long blk0 = sk * a.n_parts;
+  const float* accp = a.ws_acc + blk0 * a.group * D + 16 * hc * D + 4 * (q4 * gc + r16);
+  const float2* mlp = a.ws_ml + blk0 * a.group + 16 * hc + r16;
+  const long long acc_stride = (long long)a.group * D;  // floats between partitions
+
+  // pass 1: the running max over the partials (independent loads)
   float M = -INFINITY;
   bool nan = false;
-  for (int k = lane; k < np; k += 64) {
-    const float m = ml[k].x;
+#pragma unroll 4
+  for (int k = 0; k < np; k += R) {
+    const float m = mlp[(long long)k * a.group].x;
     nan |= m != m;
     M = fmaxf(M, m);
   }
+  // pass 2: l = sum l_k 2^(m_k - M), sums likewise, in partition order
+  float Ls = 0.f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  if (__any(nan)) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) o[j] = __builtin_nanf("");
-    store();
-    return;
-  }
-  float ls = 0.f;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) o[j] = 0.f;
+  for (int j = 0; j < 4 * S::E; ++j) o[j] = 0.f;
   if (M != -INFINITY) {
-    for (int k = 0; k < np; ++k) {
-      const float2 mk = ml[k];
-      const float w = fast_exp2(mk.x - M);
-      ls += mk.y * w;
+#pragma unroll 2
+    for (int k = 0; k < np; k += R) {
+      const float2 ml = mlp[(long long)k * a.group];
+      f32x4 v[S::E];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) o[j] += acc[(long long)k * D + j] * w;
+      for (int j = 0; j < S::E; ++j)
+        v[j] = *reinterpret_cast<const f32x4*>(accp + k * acc_stride + 16 * j * gc);
+      if (ml.x == -INFINITY) continue;  // an empty partial contributes nothing
+      const float w = fast_exp2(ml.x - M);
+      Ls += ml.y * w;
+#pragma unroll
+      for (int j = 0; j < S::E; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[4 * j + e] += v[j][e] * w;
     }
   }
-  const float inv = ls > 0.f ? 1.f / ls : 0.f;
+  const float inv = nan ? __builtin_nanf("") : (Ls > 0.f ? 1.f / Ls : 0.f);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) o[j] *= inv;
-  store();
+  for (int j = 0; j < 4 * S::E; ++j) o[j] *= inv;
+  store_out<BF16, S>(dst, o);
 }
 
 // Workgroups of the persistent kernel that fit on the device at once; queried
@@ -660,13 +800,25 @@ int resident_workgroups(Kernel kernel, int threads) {
 }
 
 template <bool BF16, int D, int BS>
-hipError_t launch_one(const DecodeArgs& a, int phases, hipStream_t stream) {
-  if (phases & 1) {
+hipError_t launch_one(const DecodeArgs& args, int phases, hipStream_t stream) {
+  DecodeArgs a = args;
+  const auto kernel = decode_partial_kernel<BF16, D, BS>;
+  long long wgs = resident_workgroups(kernel, kWaves * 64);
+  a.resident_waves = (int)(wgs * kWaves);
+  // few units: the direct grid; many: the persistent kernel with runs
+  a.direct = a.total_units <= 4LL * a.resident_waves;
+  if ((phases & 1) && a.direct) {
+    const long long grid = (a.total_units + kWaves - 1) / kWaves;
+    if (grid > 0) {
+      hipLaunchKernelGGL((decode_direct_kernel<BF16, D, BS>), dim3((unsigned)grid),
+                         dim3(kWaves * 64), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else if (phases & 1) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a, BS);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const auto kernel = decode_partial_kernel<BF16, D, BS>;
-    long long wgs = resident_workgroups(kernel, kWaves * 64);
     const long long need = (a.total_units + kWaves - 1) / kWaves;
     if (wgs > need) wgs = need;
     if (wgs > 0) {
@@ -676,8 +828,8 @@ hipError_t launch_one(const DecodeArgs& a, int phases, hipStream_t stream) {
     }
   }
   if ((phases & 2) && a.n_parts > 1) {
-    const long long heads = (long long)a.batch * a.num_heads;
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, BS>), dim3((unsigned)((heads + 3) / 4)),
+    const long long groups = (long long)a.batch * a.num_kv_heads * a.head_chunks;
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, BS>), dim3((unsigned)((groups + 3) / 4)),
                        dim3(256), 0, stream, a);
     return hipGetLastError();
   }

@@ -201,6 +201,12 @@ int decode_impl(int phases, int dtype, const void* q, void* k_cache, void* v_cac
   a.has_new = has_new;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.total_units = (long long)batch * p.n_parts * num_kv_heads * p.head_chunks;
+  // a work item may stream up to 8 consecutive partitions, within the table
+  // slice one wave stages
+  const int slice_runs = kMaxPartitionBlocks / (p.part_tokens / block_size);
+  a.max_run = slice_runs < 1 ? 1 : (slice_runs > 8 ? 8 : slice_runs);
+  a.resident_waves = 1;
+  a.direct = 0;
   if (a.total_units >= (1LL << 31)) return PKV_EUNSUPPORTED;
   hipError_t e = pkv::launch_decode(dtype, head_dim, block_size, a, phases, (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;

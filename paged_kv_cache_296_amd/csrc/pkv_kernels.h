@@ -16,10 +16,13 @@ struct DecodeArgs {
   const void* k_new;
   const void* v_new;
   void* out;
-  float* ws_acc;      // [batch, num_heads, n_parts, head_dim] unnormalised sums
-  float2* ws_ml;      // [batch, num_heads, n_parts] (running max, sum of exponentials)
+  float* ws_acc;      // [batch, num_kv_heads, n_parts, group * head_dim] unnormalised sums
+  float2* ws_ml;      // [batch, num_kv_heads, n_parts, group] (running max, sum of exponentials)
   int* ctrl;          // [0] ticket counter, [1] number of work items (written by the plan kernel)
-  int4* items;        // [batch * n_parts] work items (sequence, partition, cached length, 0)
+  int4* items;        // [batch * n_parts] work items (sequence, first partition << 8 | count, cached length, 0)
+  int max_run;        // most partitions one work item may stream (slice bound, <= 255)
+  int resident_waves; // waves of the persistent kernel resident at once
+  int direct;         // 1: one wave per grid slot (small batches), 0: persistent + work list
   int32_t* err_flag;  // may be null
   int batch, num_heads, num_kv_heads, group;  // group = num_heads / num_kv_heads
   int head_chunks;    // ceil(group / 16): a wave covers at most 16 q heads

@@ -287,3 +287,18 @@ def test_two_phase_calls_equal_decode_bitwise():
                            out=out, workspace=ws)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(kc.view(torch.int16), case.k_cache.view(torch.int16))
+
+
+@pytest.mark.parametrize("pt", [16, 32])
+def test_runs_of_partitions(pt):
+    """Enough partitions that the work list streams several consecutive
+    partitions per unit; tiny partitions put a boundary every tile or two,
+    and lengths that are multiples of the partition make the new token open
+    a partition of its own."""
+    lengths = np.random.default_rng(pt).integers(1, 1500, size=64)
+    lengths[:8] = [pt, 2 * pt, 3 * pt, 160, 320, 1024, 1008, 1]
+    case = workloads.make_decode(seed=7400 + pt, dtype="bf16", batch=64, num_heads=16,
+                                 num_kv_heads=8, head_dim=128, block_size=16,
+                                 lengths=lengths.tolist(), num_blocks=8000, append=True,
+                                 partition_tokens=pt, device=DEV)
+    run_case(case, "bf16")
