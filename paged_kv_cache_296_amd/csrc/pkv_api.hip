@@ -256,7 +256,7 @@ int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
   if (batch == 0 || total_q == 0) return PKV_OK;
   if (!q || !out || !cu_seq_lens_q || !cu_seq_lens_k || (total_k > 0 && (!k || !v)))
     return PKV_EINVAL;
-  const int rows = pkv::varlen_rows_per_workgroup();
+  const int rows = pkv::varlen_rows_per_workgroup(num_heads / num_kv_heads);
   const long long tiles = ((long long)max_length_q + rows - 1) / rows;
   if (tiles > 65535 || batch > 65535 || num_heads > 65535) return PKV_EUNSUPPORTED;
   pkv::VarlenArgs a;
@@ -275,6 +275,7 @@ int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
   a.group = num_heads / num_kv_heads;
   a.max_len_q = max_length_q;
   a.max_len_k = max_length_k;
+  a.heads_per_wg = pkv::varlen_heads_per_workgroup(a.group);
   a.q_tiles = (int)tiles;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipError_t e = pkv::launch_varlen(dtype, head_dim, a, (hipStream_t)stream);

@@ -44,6 +44,7 @@ struct VarlenArgs {
   int32_t* err_flag;
   int batch, total_q, total_k, num_heads, num_kv_heads, group;
   int max_len_q, max_len_k;
+  int heads_per_wg;   // q heads of one kv group sharing a workgroup (1, 2 or 4)
   int q_tiles;        // ceil(max_len_q / rows per workgroup)
   float scale_log2;
 };
@@ -53,6 +54,8 @@ struct VarlenArgs {
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
                          int phases, hipStream_t stream);
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
-int varlen_rows_per_workgroup();
+// Workgroup shape of the varlen kernel for a q-heads-per-kv-head ratio.
+int varlen_heads_per_workgroup(int group);
+int varlen_rows_per_workgroup(int group);
 
 }  // namespace pkv

@@ -7,19 +7,29 @@
 // of its own request; a request with no key row outputs zeros.
 //
 // How:
-//  * A workgroup (4 waves) owns 128 query rows of one q head; each wave owns
-//    32 rows.  Key tiles of 64 rows stream through LDS, double buffered: K as
-//    rows [key][dim], V transposed to [dim][key] so that both MFMA operands
-//    are 16-byte LDS reads.
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the query rows sit on the
-//    lane axis, so a row's max and sum are in-lane reductions plus one
-//    exchange between the two 32-lane halves.  P^T from the S^T accumulator
-//    is directly the B operand of O^T = V^T P^T (same MFMA), provided the key
-//    order in the V^T LDS rows swaps bits 2 and 3 of the key index, which the
-//    transposing store does.  O^T keeps one query row per lane, so the
-//    online-softmax rescale is lane-local.
-//  * Online softmax in the exp2 domain; the final division by the row sum
-//    happens once in the epilogue; bf16 output is rounded to nearest even.
+//  * A workgroup is 4 waves; each wave owns 32 query rows of one q head.  The
+//    waves of a workgroup share one kv head: with grouped heads they take up
+//    to 4 q heads of the group (same 32 rows), otherwise 4 consecutive row
+//    blocks of one head, so every K/V tile fetched is used by all 4 waves.
+//  * K and V stream through LDS in 64-key tiles, double buffered, moved from
+//    HBM straight into LDS by buffer loads with the LDS-destination bit (no
+//    register staging).  Both tiles are stored row-major, one 2*D-byte row
+//    per key, with the 16-byte chunks of a row permuted by an XOR of the row
+//    index so that the MFMA operand reads below hit distinct LDS banks.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
+//    (16-byte LDS reads), the query rows sit on the lane axis (B operand held
+//    in registers), so a row's max and sum are in-lane reductions plus one
+//    exchange between the two 32-lane halves.
+//  * O^T = V^T P^T with the same MFMA: the A operand V^T is read from the
+//    row-major V tile by ds_read_b64_tr_b16 (a transposing LDS read), and the
+//    key order of each 8-key half matches the order of the S^T accumulator,
+//    so P^T is the S^T accumulator rounded to bf16, with no data movement.
+//    O^T keeps one query row per lane, so the softmax rescale is lane-local.
+//  * Online softmax in the exp2 domain with a lazy reference: the running
+//    reference max of a row only moves (and the accumulators are rescaled)
+//    when a tile's max exceeds it by more than 2^8, so exponentials stay
+//    below 256 and most tiles skip the rescale.  The final division by the
+//    row sum happens once in the epilogue; bf16 output rounds to nearest even.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,13 +41,44 @@ namespace {
 using u32 = uint32_t;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kRows = 128;       // query rows per workgroup
+constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kWaveRows = 32;    // query rows per wave
 constexpr int kKeys = 64;        // keys per LDS tile
+constexpr float kLazy = 8.f;     // log2 of the largest exponential kept before a rescale
 constexpr unsigned kErrCu = 4u, kErrMaxLen = 8u;
+
+template <int D>
+struct Geo {
+  static constexpr int ROWB = 2 * D;                     // bytes of one key row
+  static constexpr int CH = D / 8;                       // 16-byte chunks per row
+  static constexpr int TILEB = kKeys * ROWB;             // one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;               // K tile, then V tile
+  static constexpr int NLOAD = TILEB / (1024 * kWaves);  // 1 KB loads per wave per tile
+  static constexpr int KS = D / 16;                      // 16-dim k-steps of S^T
+  static constexpr int DT = D / 32;                      // 32-dim row tiles of O^T
+};
+
+// Physical 16-byte chunk = logical chunk XOR swz(row).  For D = 128 (16
+// chunks per row) the 16 rows read together by a K operand load land on 16
+// different chunks, any 8 aligned rows on 8 different chunks modulo 8, and
+// the 4 rows x 4 chunks of one transposing V read on 16 different chunks.
+// For D = 64 (8 chunks) the K reads of 8 aligned rows and the 4 x 2 chunks of
+// a 16-lane V read are conflict free.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return ((0xCA60 >> (4 * (row & 3))) & 15) ^ ((row >> 2) & 1) ^ (row & 8);
+  else
+    return ((row & 3) << 1) | ((row >> 2) & 1);
+}
 
 __device__ __forceinline__ float swap32(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -48,105 +89,155 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
          ((u32)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
-// position of key k (0..63) inside a V^T LDS row: bits 2 and 3 swapped
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// Buffer resource of `bytes` bytes at `base` (raw, stride 0; reads past the
+// end return zeros).  base must be wave-uniform.
+__device__ __forceinline__ u32x4 vsharp(const char* base, int bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  return u32x4{(u32)p, (u32)(p >> 32) & 0xffffu, (u32)bytes, 0x00020000u};
 }
 
-template <int D>
-struct Lds {
-  static constexpr int KROW = D * 2 + 16;        // bytes per K row (padded)
-  static constexpr int VROW = kKeys * 2 + 16;    // bytes per V^T row (padded)
-  static constexpr int KBYTES = kKeys * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int BUF = KBYTES + VBYTES;
-};
-
-template <int D>
-struct Stage {
-  // K: 64 keys x D dims in 16-byte row pieces; V: groups of 4 keys x 8 dims
-  static constexpr int KPIECES = kKeys * D * 2 / 16 / 256;  // per thread
-  static constexpr int VG_TOTAL = (kKeys / 4) * (D / 8);
-  static constexpr int VGROUPS = (VG_TOTAL + 255) / 256;
-  u32x4 k[KPIECES];
-  u32x4 v[VGROUPS][4];
-};
-
-// Byte offset of (dim row r, key position p) in the V^T tile.  The 16-byte
-// chunk index (p / 8) is XOR-ed with (r / 8) mod 8 so that the transposing
-// stores, which hit rows 8 apart, spread over the LDS banks.
-template <int D>
-__device__ __forceinline__ int vt_off(int r, int p) {
-  return r * Lds<D>::VROW + 16 * ((p >> 3) ^ ((r >> 3) & 7)) + 2 * (p & 7);
+// 16 bytes per lane from buffer offset `voff` into LDS at lds_addr + 16*lane.
+// Written as inline asm so that the compiler does not see an LDS write in
+// flight: it would otherwise wait for every such load before each
+// transposing LDS read.  The loop waits for these loads itself (vmcnt(0) and
+// a barrier before a stage is read).  One wait state is needed between the
+// M0 write and the load.
+__device__ __forceinline__ void load_to_lds(u32x4 rs, int voff, u32 lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(lds_addr)
+               : "memory", "m0");
 }
 
-template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& st, const char* kg, const char* vg, int k0,
-                                           int k_end, int tok, int tid) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  // K pieces: piece p = tid + 256 * r -> key p / (D/8), 16-byte chunk p % (D/8)
+// Moves keys t0 .. t0+valid-1 (valid <= 64) of K and V into one LDS stage.
+// Lane offsets `off` address the full tile; rows past `valid` are clamped to
+// the last valid row (their scores are masked, so any finite copy will do).
+template <int D, bool PARTIAL>
+__device__ __forceinline__ void issue_tile(const char* kg, const char* vg, long long t0, int valid,
+                                           int tok, lds_char* stage, int wave, int lane,
+                                           const int* off) {
+  using G = Geo<D>;
+  const u32x4 rk = vsharp(kg + t0 * tok, valid * tok);
+  const u32x4 rv = vsharp(vg + t0 * tok, valid * tok);
 #pragma unroll
-  for (int r = 0; r < Stage<D>::KPIECES; ++r) {
-    const int p = tid + 256 * r;
-    const int key = p / (D / 8), ch = p % (D / 8);
-    const int kk = k0 + key;
-    st.k[r] = kk < k_end ? *reinterpret_cast<const u32x4*>(kg + (long long)kk * tok + 16 * ch) : z;
+  for (int i = 0; i < G::NLOAD; ++i) {
+    int o = off[i];
+    if (PARTIAL) o -= max(((wave * G::NLOAD + i) * 64 + lane) / G::CH - (valid - 1), 0) * tok;
+    const u32 dst = (u32)(uintptr_t)(stage + (wave * G::NLOAD + i) * 1024);
+    load_to_lds(rk, o, dst);
+    load_to_lds(rv, o, dst + G::TILEB);
   }
-  // V groups: g = tid + 256 * r -> dim group g % (D/8), key quad g / (D/8)
+}
+
+// One 64-key tile for one wave: S^T, softmax update, O^T += V^T P^T.
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_compute(const char* kt, lds_char* vt, const u32x4* qr,
+                                             f32x16* acc, float& m_ref, float& l_run, float c,
+                                             int valid, int hh, const int* koff, const int* voff) {
+  using G = Geo<D>;
+  // 16 MFMAs over (k-step, key block) with the K operand read four steps
+  // ahead; the scheduling fences keep the reads from all being hoisted at
+  // once, which would cost 64 registers.
+  f32x16 s[2];
 #pragma unroll
-  for (int r = 0; r < Stage<D>::VGROUPS; ++r) {
-    const int g = tid + 256 * r;
-    const int dg = g % (D / 8), kq = g / (D / 8);
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = k0 + 4 * kq + i;
-      st.v[r][i] = (g < Stage<D>::VG_TOTAL && kk < k_end)
-                       ? *reinterpret_cast<const u32x4*>(vg + (long long)kk * tok + 16 * dg)
-                       : z;
+    for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+  constexpr int NQK = 2 * G::KS;
+  u32x4 kf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    kf[i] = *reinterpret_cast<const u32x4*>(kt + koff[i >> 1] + 32 * (i & 1) * G::ROWB);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[i & 3]),
+                                                       __builtin_bit_cast(bf16x8, qr[i >> 1]),
+                                                       s[i & 1], 0, 0, 0);
+    if (i + 4 < NQK)
+      kf[i & 3] = *reinterpret_cast<const u32x4*>(kt + koff[(i + 4) >> 1] +
+                                                  32 * (i & 1) * G::ROWB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // key of accumulator element r of block mt: 32 mt + 8 (r / 4) + 4 hh + r % 4
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = !MASK || 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3) < valid;
+      mx = fmaxf(mx, ok ? s[mt][r] : -INFINITY);
     }
+  mx = fmaxf(mx, swap32(mx));
+  const float ms = mx * c;
+  if (__builtin_amdgcn_ballot_w64(ms > m_ref + kLazy) != 0) {
+    const float mn = fmaxf(m_ref, ms);
+    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref - mn);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < G::DT; ++d) acc[d] *= alpha;
+    m_ref = mn;
   }
-}
-
-template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D>& st, char* buf, int tid) {
+  const float neg_m = -m_ref;
+  float psum = 0.f;
+  u32 pw[2][8];
 #pragma unroll
-  for (int r = 0; r < Stage<D>::KPIECES; ++r) {
-    const int p = tid + 256 * r;
-    const int key = p / (D / 8), ch = p % (D / 8);
-    *reinterpret_cast<u32x4*>(buf + key * Lds<D>::KROW + 16 * ch) = st.k[r];
-  }
-  char* vt = buf + Lds<D>::KBYTES;
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-  for (int r = 0; r < Stage<D>::VGROUPS; ++r) {
-    const int g = tid + 256 * r;
-    if (g >= Stage<D>::VG_TOTAL) break;
-    const int dg = g % (D / 8), kq = g / (D / 8);
-    const int pos = vt_pos(4 * kq);  // the 4 keys stay adjacent
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      u32 t01, t23;
-      if (e & 1) {
-        t01 = (st.v[r][0][w] >> 16) | (st.v[r][1][w] & 0xffff0000u);
-        t23 = (st.v[r][2][w] >> 16) | (st.v[r][3][w] & 0xffff0000u);
-      } else {
-        t01 = (st.v[r][0][w] & 0xffffu) | (st.v[r][1][w] << 16);
-        t23 = (st.v[r][2][w] & 0xffffu) | (st.v[r][3][w] << 16);
+    for (int r = 0; r < 16; r += 2) {
+      float x0 = fmaf(s[mt][r], c, neg_m), x1 = fmaf(s[mt][r + 1], c, neg_m);
+      if (MASK) {
+        const int key = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        x0 = key < valid ? x0 : -INFINITY;
+        x1 = key + 1 < valid ? x1 : -INFINITY;
       }
-      *reinterpret_cast<u32x2*>(vt + vt_off<D>(8 * dg + e, pos)) = u32x2{t01, t23};
+      const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
+      psum += p0 + p1;
+      pw[mt][r >> 1] = pack_bf16x2(p0, p1);
     }
+  l_run += psum;
+
+  // 16 keys per step: this lane's P^T operand holds keys 16 kc + 4 hh + {0..3}
+  // and 16 kc + 8 + 4 hh + {0..3}, the two transposing reads fetch V^T for
+  // exactly those keys.  The reads run two MFMAs ahead.
+  constexpr int NPV = 4 * G::DT;
+  auto vread = [&](int i) {
+    const int kc = i / G::DT, d = i % G::DT;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vt + voff[2 * d] + 16 * kc * G::ROWB));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vt + voff[2 * d + 1] + 16 * kc * G::ROWB));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  i16x8 vf[2];
+  vf[0] = vread(0);
+  vf[1] = vread(1);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    const int kc = i / G::DT, d = i % G::DT;
+    const int mt = kc >> 1, ap = kc & 1;
+    const u32x4 pf = {pw[mt][4 * ap], pw[mt][4 * ap + 1], pw[mt][4 * ap + 2], pw[mt][4 * ap + 3]};
+    acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[i & 1]),
+                                                     __builtin_bit_cast(bf16x8, pf), acc[d],
+                                                     0, 0, 0);
+    if (i + 2 < NPV) vf[i & 1] = vread(i + 2);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void varlen_kernel(VarlenArgs a) {
-  constexpr int KS = D / 16;     // QK k-steps of 16 dims
-  constexpr int DT = D / 32;     // O^T dim tiles
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void varlen_kernel(VarlenArgs a) {
+  using G = Geo<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps row math scalar
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n = lane & 31, hh = lane >> 5;
+  const int hpw = a.heads_per_wg, rb = kWaves / hpw;
+  const int hw = wave % hpw, rbi = wave / hpw;
+  const int qt = blockIdx.x, b = blockIdx.z;
+  const int h0 = blockIdx.y * hpw;
+  const int wg_rows = kWaveRows * rb;
 
   const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
   const int k0s = a.cu_k[b], k1s = a.cu_k[b + 1];
@@ -156,123 +247,107 @@ __global__ __launch_bounds__(256) void varlen_kernel(VarlenArgs a) {
                      (b != a.batch - 1 || (q1 == a.total_q && k1s == a.total_k));
   const bool len_ok = len_q <= a.max_len_q && len_k <= a.max_len_k;
   if (!cu_ok || !len_ok) {
-    if (a.err_flag && tid == 0 && qt == 0 && h == 0) atomicOr(a.err_flag, (int)(cu_ok ? kErrMaxLen : kErrCu));
+    if (a.err_flag && tid == 0 && qt == 0 && blockIdx.y == 0)
+      atomicOr(a.err_flag, (int)(cu_ok ? kErrMaxLen : kErrCu));
     if (!(q0 >= 0 && q1 >= q0 && q1 <= a.total_q)) return;  // nowhere safe to write
-    for (int r = qt * kRows + tid; r < min(len_q, (qt + 1) * kRows); r += 256) {
-      __bf16* o = (__bf16*)a.out + ((long long)(q0 + r) * a.num_heads + h) * D;
+    const int r0 = qt * wg_rows, r1 = min(len_q, r0 + wg_rows);
+    for (int i = tid; i < (r1 > r0 ? (r1 - r0) * hpw : 0); i += 256) {
+      const int r = r0 + i / hpw, hq = h0 + i % hpw;
+      __bf16* o = (__bf16*)a.out + ((long long)(q0 + r) * a.num_heads + hq) * D;
       for (int d = 0; d < D; ++d) o[d] = (__bf16)__builtin_nanf("");
     }
     return;
   }
-  if (qt * kRows >= len_q) return;
+  if (qt * wg_rows >= len_q) return;
 
-  const int kvh = h / a.group;
+  const int h = h0 + hw;
+  const int kvh = h0 / a.group;
   const int tok_q = a.num_heads * D * 2;     // bytes between query rows
   const int tok_k = a.num_kv_heads * D * 2;  // bytes between key rows
   const char* kg = (const char*)a.k + (long long)k0s * tok_k + (long long)kvh * D * 2;
   const char* vg = (const char*)a.v + (long long)k0s * tok_k + (long long)kvh * D * 2;
+  lds_char* lds = (lds_char*)smem;
 
-  // this lane's query row as the B operand: dims 16s + 8hh + j
-  const int row = qt * kRows + wave * kWaveRows + n;
+  // this lane's query row as the B operand: dims 16 s + 8 hh + 0..7; a
+  // negative scale is folded into q (a sign flip is exact in bf16)
+  const int row = qt * wg_rows + rbi * kWaveRows + n;
   const bool row_ok = row < len_q;
-  const bool wave_active = qt * kRows + wave * kWaveRows < len_q;
-  u32x4 qr[KS];
+  const bool wave_active = qt * wg_rows + rbi * kWaveRows < len_q;
+  const u32 sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float c = fabsf(a.scale_log2);
+  u32x4 qr[G::KS];
   {
-    const char* qp = (const char*)a.q + (long long)(q0 + (row_ok ? row : 0)) * tok_q + (long long)h * D * 2 + 16 * hh;
+    const char* qp = (const char*)a.q + (long long)(q0 + (row_ok ? row : 0)) * tok_q +
+                     (long long)h * D * 2 + 16 * hh;
+    const u32 keep = row_ok ? ~0u : 0u;  // rows past the end read row 0, then zero
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      qr[s] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * s) : z;
-    }
+    for (int s = 0; s < G::KS; ++s)
+      qr[s] = (*reinterpret_cast<const u32x4*>(qp + 32 * s) ^ sign) & keep;
   }
 
-  f32x16 acc[DT];
+  // lane offsets: tile loads (same for K and V), K operand reads, V^T reads
+  int loff[G::NLOAD];
 #pragma unroll
-  for (int d = 0; d < DT; ++d)
+  for (int i = 0; i < G::NLOAD; ++i) {
+    const int cl = (wave * G::NLOAD + i) * 64 + lane;
+    const int r = cl / G::CH, ps = cl % G::CH;
+    loff[i] = r * tok_k + 16 * (ps ^ swz<D>(r));
+  }
+  int koff[G::KS];
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) koff[ks] = n * G::ROWB + 16 * ((2 * ks + hh) ^ swz<D>(n));
+  int voff[2 * G::DT];
+  {
+    const int q16 = lane & 15, grp = (lane >> 4) & 1;
+#pragma unroll
+    for (int d = 0; d < G::DT; ++d)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int vr = 8 * r + 4 * hh + (q16 >> 2);
+        const int lc = 4 * d + 2 * grp + ((q16 >> 1) & 1);
+        voff[2 * d + r] = G::TILEB + vr * G::ROWB + 16 * (lc ^ swz<D>(vr)) + 8 * (q16 & 1);
+      }
+  }
+
+  f32x16 acc[G::DT];
+#pragma unroll
+  for (int d = 0; d < G::DT; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
   const int nk = (len_k + kKeys - 1) / kKeys;
-  Stage<D> st;
-  if (nk > 0) {
-    stage_load<D>(st, kg, vg, 0, len_k, tok_k, tid);
-    stage_store<D>(st, smem, tid);
-  }
-  __syncthreads();
+  const int last_valid = len_k - (nk - 1) * kKeys;  // keys in the last tile
+  auto issue = [&](int j) {
+    lds_char* st = lds + (j & 1) * G::STAGEB;
+    if (j + 1 < nk || last_valid == kKeys)
+      issue_tile<D, false>(kg, vg, (long long)j * kKeys, kKeys, tok_k, st, wave, lane, loff);
+    else
+      issue_tile<D, true>(kg, vg, (long long)j * kKeys, last_valid, tok_k, st, wave, lane, loff);
+  };
+  if (nk > 0) issue(0);
   for (int j = 0; j < nk; ++j) {
-    char* cur = smem + (j & 1) * Lds<D>::BUF;
-    if (j + 1 < nk) stage_load<D>(st, kg, vg, (j + 1) * kKeys, len_k, tok_k, tid);
-    if (wave_active) {
-      // S^T for two 32-key tiles
-      f32x16 s[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-        const char* kp = cur + (32 * mt + n) * Lds<D>::KROW + 16 * hh;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                          __builtin_bit_cast(bf16x8, qr[ks]), s[mt], 0, 0, 0);
-        }
-      }
-      // scale, mask the key tail, row max
-      const int kbase = j * kKeys;
-      float mt_max = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float x = s[mt][r] * a.scale_log2;
-          if (key >= len_k) x = -INFINITY;
-          s[mt][r] = x;
-          mt_max = fmaxf(mt_max, x);
-        }
-      mt_max = fmaxf(mt_max, swap32(mt_max));
-      const float m_new = fmaxf(m_run, mt_max);
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
-      u32 pw[2][8];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(s[mt][r] - m_new), p1 = fast_exp2(s[mt][r + 1] - m_new);
-          psum += p0 + p1;
-          pw[mt][r >> 1] = pack_bf16x2(p0, p1);
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) acc[d] *= alpha;
-      // O^T += V^T P^T, 16 keys per step
-      const char* vt = cur + Lds<D>::KBYTES;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int mt = kk >> 1, ap = kk & 1;
-        const u32x4 pf = {pw[mt][4 * ap], pw[mt][4 * ap + 1], pw[mt][4 * ap + 2], pw[mt][4 * ap + 3]};
-#pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(
-              vt + vt_off<D>(32 * d + n, 32 * mt + 16 * ap + 8 * hh));
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
-                                                           __builtin_bit_cast(bf16x8, pf), acc[d], 0, 0, 0);
-        }
-      }
-    }
-    if (j + 1 < nk) stage_store<D>(st, smem + ((j + 1) & 1) * Lds<D>::BUF, tid);
+    // own loads of tile j done, then everyone's; this also retires every
+    // wave's reads of tile j-1, whose stage the next issue overwrites
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
+    if (j + 1 < nk) issue(j + 1);
+    if (!wave_active) continue;
+    const char* kt = smem + (j & 1) * G::STAGEB;
+    lds_char* vt = lds + (j & 1) * G::STAGEB;
+    if (j + 1 < nk || last_valid == kKeys)
+      tile_compute<D, false>(kt, vt, qr, acc, m_ref, l_run, c, kKeys, hh, koff, voff);
+    else
+      tile_compute<D, true>(kt, vt, qr, acc, m_ref, l_run, c, last_valid, hh, koff, voff);
   }
 
   if (!row_ok) return;
-  float l_tot = l_run + swap32(l_run);
+  const float l_tot = l_run + swap32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   char* op = (char*)a.out + (long long)(q0 + row) * tok_q + (long long)h * D * 2;
+  // O^T element r of row tile d is dim 32 d + 8 (r / 4) + 4 hh + r % 4
 #pragma unroll
-  for (int d = 0; d < DT; ++d)
+  for (int d = 0; d < G::DT; ++d)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dim = 32 * d + 8 * g + 4 * hh;
@@ -284,7 +359,7 @@ __global__ __launch_bounds__(256) void varlen_kernel(VarlenArgs a) {
 
 template <int D>
 hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
-  const size_t lds = 2 * Lds<D>::BUF;
+  const size_t lds = 2 * Geo<D>::STAGEB;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)varlen_kernel<D>,
@@ -292,14 +367,20 @@ hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(varlen_kernel<D>, dim3(a.q_tiles, a.num_heads, a.batch), dim3(256), lds,
-                     stream, a);
+  hipLaunchKernelGGL(varlen_kernel<D>, dim3(a.q_tiles, a.num_heads / a.heads_per_wg, a.batch),
+                     dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int varlen_rows_per_workgroup() { return kRows; }
+int varlen_heads_per_workgroup(int group) {
+  return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
+int varlen_rows_per_workgroup(int group) {
+  return kWaveRows * (kWaves / varlen_heads_per_workgroup(group));
+}
 
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream) {
   if (dtype != 1) return hipErrorInvalidValue;
