@@ -44,6 +44,8 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -80,13 +82,23 @@ __device__ __forceinline__ int swz(int row) {
     return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
-__device__ __forceinline__ float swap32(float x) { return __shfl_xor(x, 32, 64); }
+// x of lane l and of lane l ^ 32 (in either order) by one v_permlane32_swap;
+// max and + of the pair are then the same in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (u32)__builtin_bit_cast(unsigned short, a) |
-         ((u32)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Buffer resource of `bytes` bytes at `base` (raw, stride 0; reads past the
@@ -159,16 +171,21 @@ __device__ __forceinline__ void tile_compute(const char* kt, lds_char* vt, const
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // key of accumulator element r of block mt: 32 mt + 8 (r / 4) + 4 hh + r % 4
+  // key of accumulator element r of block mt: 32 mt + 8 (r / 4) + 4 hh + r % 4;
+  // keys past the end score -inf (c > 0, so they give exp2(-inf) = 0)
+  if (MASK) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3) >= valid) s[mt][r] = -INFINITY;
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok = !MASK || 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3) < valid;
-      mx = fmaxf(mx, ok ? s[mt][r] : -INFINITY);
-    }
-  mx = fmaxf(mx, swap32(mx));
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+  mx = pair_max(mx);
   const float ms = mx * c;
   if (__builtin_amdgcn_ballot_w64(ms > m_ref + kLazy) != 0) {
     const float mn = fmaxf(m_ref, ms);
@@ -185,13 +202,8 @@ __device__ __forceinline__ void tile_compute(const char* kt, lds_char* vt, const
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float x0 = fmaf(s[mt][r], c, neg_m), x1 = fmaf(s[mt][r + 1], c, neg_m);
-      if (MASK) {
-        const int key = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        x0 = key < valid ? x0 : -INFINITY;
-        x1 = key + 1 < valid ? x1 : -INFINITY;
-      }
-      const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
+      const float p0 = fast_exp2(fmaf(s[mt][r], c, neg_m));
+      const float p1 = fast_exp2(fmaf(s[mt][r + 1], c, neg_m));
       psum += p0 + p1;
       pw[mt][r >> 1] = pack_bf16x2(p0, p1);
     }
@@ -273,13 +285,15 @@ void varlen_kernel(VarlenArgs a) {
   const int row = qt * wg_rows + rbi * kWaveRows + n;
   const bool row_ok = row < len_q;
   const bool wave_active = qt * wg_rows + rbi * kWaveRows < len_q;
+  // c > 0 always: a zero scale zeroes q instead (every score is then 0)
   const u32 sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  const float c = fabsf(a.scale_log2);
+  const float c = a.scale_log2 == 0.f ? 1.f : fabsf(a.scale_log2);
   u32x4 qr[G::KS];
   {
     const char* qp = (const char*)a.q + (long long)(q0 + (row_ok ? row : 0)) * tok_q +
                      (long long)h * D * 2 + 16 * hh;
-    const u32 keep = row_ok ? ~0u : 0u;  // rows past the end read row 0, then zero
+    // rows past the end read row 0, then zero
+    const u32 keep = row_ok && a.scale_log2 != 0.f ? ~0u : 0u;
 #pragma unroll
     for (int s = 0; s < G::KS; ++s)
       qr[s] = (*reinterpret_cast<const u32x4*>(qp + 32 * s) ^ sign) & keep;
@@ -325,6 +339,9 @@ void varlen_kernel(VarlenArgs a) {
     else
       issue_tile<D, true>(kg, vg, (long long)j * kKeys, last_valid, tok_k, st, wave, lane, loff);
   };
+  // full tiles in the loop; a partial last tile is peeled off after it so
+  // the loop body has one code path (and one register assignment)
+  const bool partial = last_valid < kKeys;
   if (nk > 0) issue(0);
   for (int j = 0; j < nk; ++j) {
     // own loads of tile j done, then everyone's; this also retires every
@@ -332,17 +349,18 @@ void varlen_kernel(VarlenArgs a) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
     if (j + 1 < nk) issue(j + 1);
-    if (!wave_active) continue;
-    const char* kt = smem + (j & 1) * G::STAGEB;
-    lds_char* vt = lds + (j & 1) * G::STAGEB;
-    if (j + 1 < nk || last_valid == kKeys)
-      tile_compute<D, false>(kt, vt, qr, acc, m_ref, l_run, c, kKeys, hh, koff, voff);
-    else
-      tile_compute<D, true>(kt, vt, qr, acc, m_ref, l_run, c, last_valid, hh, koff, voff);
+    if (!wave_active || (partial && j + 1 == nk)) continue;
+    tile_compute<D, false>(smem + (j & 1) * G::STAGEB, lds + (j & 1) * G::STAGEB, qr, acc, m_ref,
+                           l_run, c, kKeys, hh, koff, voff);
+  }
+  if (wave_active && nk > 0 && partial) {
+    const int j = nk - 1;
+    tile_compute<D, true>(smem + (j & 1) * G::STAGEB, lds + (j & 1) * G::STAGEB, qr, acc, m_ref,
+                          l_run, c, last_valid, hh, koff, voff);
   }
 
   if (!row_ok) return;
-  const float l_tot = l_run + swap32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   char* op = (char*)a.out + (long long)(q0 + row) * tok_q + (long long)h * D * 2;
   // O^T element r of row tile d is dim 32 d + 8 (r / 4) + 4 hh + r % 4

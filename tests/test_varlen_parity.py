@@ -3,7 +3,9 @@
 Covers the HF page's worked example (a request with no key, one with a single
 key, one with seven), the 16-sequence prefill batch at full size (sampled
 rows for the oracle), the 8 x 1024 prefill of the mixed step, and small cases
-with ragged tails, empty requests, head_dim 64/128 and group sizes 1..8.
+with ragged tails, empty requests, head_dim 64/128, group sizes 1..8 (each
+workgroup packing of q heads), negative / zero / large softmax scales and
+scores whose row max keeps moving across key tiles.
 """
 import numpy as np
 import pytest
@@ -72,13 +74,45 @@ def test_mixed_step_prefill_sampled():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("group", [1, 4, 8])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 6, 8])
 def test_small_ragged(D, group):
     lq = [0, 1, 5, 31, 32, 33, 127, 128, 129, 200, 300]
     lk = [3, 0, 70, 64, 65, 1, 127, 128, 129, 500, 63]
     case = workloads.make_varlen(seed=4100 + D + group, dtype="bf16", batch=len(lq),
                                  num_heads=2 * group, num_kv_heads=2, head_dim=D,
                                  q_lengths=lq, k_lengths=lk, device=DEV)
+    run_case(case)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 4.0])
+def test_softmax_scale_sign_and_size(scale):
+    """Negative, zero and large scales.  Zero makes every row the plain mean
+    of its sequence's V rows, checked against numpy as well as the oracle."""
+    lq, lk = [33, 70, 5], [200, 64, 129]
+    case = workloads.make_varlen(seed=4400, dtype="bf16", batch=3, num_heads=8, num_kv_heads=2,
+                                 head_dim=128, q_lengths=lq, k_lengths=lk, device=DEV,
+                                 softmax_scale=scale)
+    out, _ = run_case(case)
+    if scale == 0.0:
+        v = gpu_to_f64(case.v)[0]
+        o = gpu_to_f64(out)[0]
+        ck, cq = np.cumsum([0] + lk), np.cumsum([0] + lq)
+        for b in range(3):
+            mean = v[ck[b]:ck[b + 1]].mean(axis=0)          # [kv heads, D]
+            want = np.repeat(mean, 4, axis=0)                # q head h reads kv head h // 4
+            assert np.abs(o[cq[b]:cq[b + 1]] - want[None]).max() < 1e-2
+
+
+def test_rising_and_falling_scores_across_tiles():
+    """Key rows scaled so the row max climbs (and later falls) tile after
+    tile: the running softmax reference has to move many times."""
+    case = workloads.make_varlen(seed=4500, dtype="bf16", batch=2, num_heads=4, num_kv_heads=1,
+                                 head_dim=128, q_lengths=[64, 40], k_lengths=[1500, 700],
+                                 device=DEV, softmax_scale=0.5)
+    n = case.k.shape[1]
+    ramp = torch.linspace(0.05, 3.0, n, device=DEV)
+    ramp[n // 2:] = ramp[n // 2:].flip(0)
+    case.k.mul_(ramp.view(1, n, 1, 1).to(case.k.dtype))
     run_case(case)
 
 
