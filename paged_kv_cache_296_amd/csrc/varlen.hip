@@ -62,7 +62,6 @@ struct Geo {
   static constexpr int ROWB = 2 * D;                     // bytes of one key row
   static constexpr int CH = D / 8;                       // 16-byte chunks per row
   static constexpr int TILEB = kKeys * ROWB;             // one K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;               // K tile, then V tile
   static constexpr int NLOAD = TILEB / (1024 * kWaves);  // 1 KB loads per wave per tile
   static constexpr int KS = D / 16;                      // 16-dim k-steps of S^T
   static constexpr int DT = D / 32;                      // 32-dim row tiles of O^T
@@ -121,56 +120,35 @@ __device__ __forceinline__ void load_to_lds(u32x4 rs, int voff, u32 lds_addr) {
                : "memory", "m0");
 }
 
-// Moves keys t0 .. t0+valid-1 (valid <= 64) of K and V into one LDS stage.
+// Moves rows t0 .. t0+valid-1 (valid <= 64) of K or V into one LDS tile.
 // Lane offsets `off` address the full tile; rows past `valid` are clamped to
 // the last valid row (their scores are masked, so any finite copy will do).
 template <int D, bool PARTIAL>
-__device__ __forceinline__ void issue_tile(const char* kg, const char* vg, long long t0, int valid,
-                                           int tok, lds_char* stage, int wave, int lane,
-                                           const int* off) {
+__device__ __forceinline__ void issue_tile(const char* g, long long t0, int valid, int tok,
+                                           lds_char* tile, int wave, int lane, const int* off) {
   using G = Geo<D>;
-  const u32x4 rk = vsharp(kg + t0 * tok, valid * tok);
-  const u32x4 rv = vsharp(vg + t0 * tok, valid * tok);
+  const u32x4 rs = vsharp(g + t0 * tok, valid * tok);
 #pragma unroll
   for (int i = 0; i < G::NLOAD; ++i) {
     int o = off[i];
     if (PARTIAL) o -= max(((wave * G::NLOAD + i) * 64 + lane) / G::CH - (valid - 1), 0) * tok;
-    const u32 dst = (u32)(uintptr_t)(stage + (wave * G::NLOAD + i) * 1024);
-    load_to_lds(rk, o, dst);
-    load_to_lds(rv, o, dst + G::TILEB);
+    load_to_lds(rs, o, (u32)(uintptr_t)(tile + (wave * G::NLOAD + i) * 1024));
   }
 }
 
-// One 64-key tile for one wave: S^T, softmax update, O^T += V^T P^T.
-template <int D, bool MASK>
-__device__ __forceinline__ void tile_compute(const char* kt, lds_char* vt, const u32x4* qr,
-                                             f32x16* acc, float& m_ref, float& l_run, float c,
-                                             int valid, int hh, const int* koff, const int* voff) {
-  using G = Geo<D>;
-  // 16 MFMAs over (k-step, key block) with the K operand read four steps
-  // ahead; the scheduling fences keep the reads from all being hoisted at
-  // once, which would cost 64 registers.
-  f32x16 s[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-  constexpr int NQK = 2 * G::KS;
-  u32x4 kf[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    kf[i] = *reinterpret_cast<const u32x4*>(kt + koff[i >> 1] + 32 * (i & 1) * G::ROWB);
-#pragma unroll
-  for (int i = 0; i < NQK; ++i) {
-    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[i & 3]),
-                                                       __builtin_bit_cast(bf16x8, qr[i >> 1]),
-                                                       s[i & 1], 0, 0, 0);
-    if (i + 4 < NQK)
-      kf[i & 3] = *reinterpret_cast<const u32x4*>(kt + koff[(i + 4) >> 1] +
-                                                  32 * (i & 1) * G::ROWB);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+// Reads the K operand of step i of S^T = K Q^T: k-step i / 2, key block i % 2.
+template <int D>
+__device__ __forceinline__ u32x4 k_operand(const char* kt, const int* koff, int i) {
+  return *reinterpret_cast<const u32x4*>(kt + koff[i >> 1] + 32 * (i & 1) * Geo<D>::ROWB);
+}
 
+// Masks keys past `valid` (MASK), takes the row max of the tile's scores and
+// moves the lazy softmax reference when the max has run more than 2^8 past
+// it (rescaling l and the O^T accumulators).  Returns -reference.
+template <int D, bool MASK>
+__device__ __forceinline__ float softmax_head(f32x16 (&s)[2], f32x16* acc, float& m_ref,
+                                              float& l_run, float c, int valid, int hh) {
+  using G = Geo<D>;
   // key of accumulator element r of block mt: 32 mt + 8 (r / 4) + 4 hh + r % 4;
   // keys past the end score -inf (c > 0, so they give exp2(-inf) = 0)
   if (MASK) {
@@ -195,23 +173,80 @@ __device__ __forceinline__ void tile_compute(const char* kt, lds_char* vt, const
     for (int d = 0; d < G::DT; ++d) acc[d] *= alpha;
     m_ref = mn;
   }
-  const float neg_m = -m_ref;
-  float psum = 0.f;
-  u32 pw[2][8];
+  return -m_ref;
+}
+
+// Exponentials of elements 2e, 2e+1 of the flattened scores, packed to bf16.
+__device__ __forceinline__ void exp_pair(const f32x16 (&s)[2], int e, float c, float neg_m,
+                                         float& psum, u32 (&pw)[2][8]) {
+  const int mt = e >> 3, r = 2 * (e & 7);
+  const float p0 = fast_exp2(fmaf(s[mt][r], c, neg_m));
+  const float p1 = fast_exp2(fmaf(s[mt][r + 1], c, neg_m));
+  psum += p0 + p1;
+  pw[mt][r >> 1] = pack_bf16x2(p0, p1);
+}
+
+// S^T of the next tile (16 MFMAs, K operand read four steps ahead) with the
+// exponentials of the current tile spread between them, so that the matrix
+// core and the vector ALU of one wave work at the same time.  The scheduling
+// fences keep this interleaving and keep the K reads from all being hoisted.
+template <int D>
+__device__ __forceinline__ void qk_and_exp(const char* kt, const u32x4* qr, const int* koff,
+                                           f32x16 (&sn)[2], const f32x16 (&sc)[2], float c,
+                                           float neg_m, float& psum, u32 (&pw)[2][8]) {
+  using G = Geo<D>;
+  constexpr int NQK = 2 * G::KS;
+  constexpr int EPS = 16 / NQK;  // exponential pairs per MFMA
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(s[mt][r], c, neg_m));
-      const float p1 = fast_exp2(fmaf(s[mt][r + 1], c, neg_m));
-      psum += p0 + p1;
-      pw[mt][r >> 1] = pack_bf16x2(p0, p1);
-    }
-  l_run += psum;
+    for (int r = 0; r < 16; ++r) sn[mt][r] = 0.f;
+  u32x4 kf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kf[i] = k_operand<D>(kt, koff, i);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[i & 3]),
+                                                        __builtin_bit_cast(bf16x8, qr[i >> 1]),
+                                                        sn[i & 1], 0, 0, 0);
+    if (i + 4 < NQK) kf[i & 3] = k_operand<D>(kt, koff, i + 4);
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) exp_pair(sc, EPS * i + e, c, neg_m, psum, pw);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
-  // 16 keys per step: this lane's P^T operand holds keys 16 kc + 4 hh + {0..3}
-  // and 16 kc + 8 + 4 hh + {0..3}, the two transposing reads fetch V^T for
-  // exactly those keys.  The reads run two MFMAs ahead.
+// S^T of one tile alone (the first tile).
+template <int D>
+__device__ __forceinline__ void qk_only(const char* kt, const u32x4* qr, const int* koff,
+                                        f32x16 (&sn)[2]) {
+  using G = Geo<D>;
+  constexpr int NQK = 2 * G::KS;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sn[mt][r] = 0.f;
+  u32x4 kf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kf[i] = k_operand<D>(kt, koff, i);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[i & 3]),
+                                                        __builtin_bit_cast(bf16x8, qr[i >> 1]),
+                                                        sn[i & 1], 0, 0, 0);
+    if (i + 4 < NQK) kf[i & 3] = k_operand<D>(kt, koff, i + 4);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// O^T += V^T P^T over the tile's 64 keys.  16 keys per step: this lane's P^T
+// operand holds keys 16 kc + 4 hh + {0..3} and 16 kc + 8 + 4 hh + {0..3}, and
+// the two transposing reads fetch V^T for exactly those keys.  The reads run
+// two MFMAs ahead.
+template <int D>
+__device__ __forceinline__ void pv(lds_char* vt, const int* voff, const u32 (&pw)[2][8],
+                                   f32x16* acc) {
+  using G = Geo<D>;
   constexpr int NPV = 4 * G::DT;
   auto vread = [&](int i) {
     const int kc = i / G::DT, d = i % G::DT;
@@ -319,7 +354,7 @@ void varlen_kernel(VarlenArgs a) {
       for (int r = 0; r < 2; ++r) {
         const int vr = 8 * r + 4 * hh + (q16 >> 2);
         const int lc = 4 * d + 2 * grp + ((q16 >> 1) & 1);
-        voff[2 * d + r] = G::TILEB + vr * G::ROWB + 16 * (lc ^ swz<D>(vr)) + 8 * (q16 & 1);
+        voff[2 * d + r] = vr * G::ROWB + 16 * (lc ^ swz<D>(vr)) + 8 * (q16 & 1);
       }
   }
 
@@ -330,33 +365,70 @@ void varlen_kernel(VarlenArgs a) {
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;
 
+  // LDS: K tiles at [0, 2 TILEB) and V tiles at [2 TILEB, 4 TILEB), double
+  // buffered by tile parity.  Iteration j reads K of tile j+1 (the next
+  // S^T) and V of tile j, and meanwhile loads K of tile j+2 and V of tile
+  // j+1 into the buffers that iteration j-1 finished with.
   const int nk = (len_k + kKeys - 1) / kKeys;
   const int last_valid = len_k - (nk - 1) * kKeys;  // keys in the last tile
-  auto issue = [&](int j) {
-    lds_char* st = lds + (j & 1) * G::STAGEB;
-    if (j + 1 < nk || last_valid == kKeys)
-      issue_tile<D, false>(kg, vg, (long long)j * kKeys, kKeys, tok_k, st, wave, lane, loff);
-    else
-      issue_tile<D, true>(kg, vg, (long long)j * kKeys, last_valid, tok_k, st, wave, lane, loff);
-  };
-  // full tiles in the loop; a partial last tile is peeled off after it so
-  // the loop body has one code path (and one register assignment)
   const bool partial = last_valid < kKeys;
-  if (nk > 0) issue(0);
-  for (int j = 0; j < nk; ++j) {
-    // own loads of tile j done, then everyone's; this also retires every
-    // wave's reads of tile j-1, whose stage the next issue overwrites
+  auto kbuf = [&](int j) { return lds + (j & 1) * G::TILEB; };
+  auto vbuf = [&](int j) { return lds + (2 + (j & 1)) * G::TILEB; };
+  auto issue = [&](const char* g, int j, lds_char* tile) {
+    if (j + 1 < nk || !partial)
+      issue_tile<D, false>(g, (long long)j * kKeys, kKeys, tok_k, tile, wave, lane, loff);
+    else
+      issue_tile<D, true>(g, (long long)j * kKeys, last_valid, tok_k, tile, wave, lane, loff);
+  };
+  auto wait_all = [&]() {
+    // own loads done, then everyone's; this also retires every wave's reads
+    // of the buffers the following issues overwrite
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
-    if (j + 1 < nk) issue(j + 1);
-    if (!wave_active || (partial && j + 1 == nk)) continue;
-    tile_compute<D, false>(smem + (j & 1) * G::STAGEB, lds + (j & 1) * G::STAGEB, qr, acc, m_ref,
-                           l_run, c, kKeys, hh, koff, voff);
-  }
-  if (wave_active && nk > 0 && partial) {
-    const int j = nk - 1;
-    tile_compute<D, true>(smem + (j & 1) * G::STAGEB, lds + (j & 1) * G::STAGEB, qr, acc, m_ref,
-                          l_run, c, last_valid, hh, koff, voff);
+  };
+  f32x16 sa[2], sb[2];
+  auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {  // tile j, with a next tile
+    wait_all();
+    if (j + 2 < nk) issue(kg, j + 2, kbuf(j));
+    issue(vg, j + 1, vbuf(j + 1));
+    if (!wave_active) return;
+    const float neg_m = softmax_head<D, false>(sc, acc, m_ref, l_run, c, kKeys, hh);
+    float psum = 0.f;
+    u32 pw[2][8];
+    qk_and_exp<D>((const char*)kbuf(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
+    l_run += psum;
+    pv<D>(vbuf(j), voff, pw, acc);
+  };
+  if (nk > 0) {
+    issue(kg, 0, kbuf(0));
+    issue(vg, 0, vbuf(0));
+    if (nk > 1) issue(kg, 1, kbuf(1));
+    wait_all();
+    if (wave_active) qk_only<D>((const char*)kbuf(0), qr, koff, sa);
+    int j = 0;
+    for (; j + 2 < nk; j += 2) {
+      step(j, sa, sb);
+      step(j + 1, sb, sa);
+    }
+    if (j + 1 < nk) {
+      step(j, sa, sb);
+      ++j;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sa[mt] = sb[mt];
+    }
+    // last tile (j = nk - 1): scores in sa, V in vbuf(j)
+    wait_all();
+    if (wave_active) {
+      const float neg_m = partial
+          ? softmax_head<D, true>(sa, acc, m_ref, l_run, c, last_valid, hh)
+          : softmax_head<D, false>(sa, acc, m_ref, l_run, c, kKeys, hh);
+      float psum = 0.f;
+      u32 pw[2][8];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) exp_pair(sa, e, c, neg_m, psum, pw);
+      l_run += psum;
+      pv<D>(vbuf(j), voff, pw, acc);
+    }
   }
 
   if (!row_ok) return;
@@ -377,7 +449,7 @@ void varlen_kernel(VarlenArgs a) {
 
 template <int D>
 hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
-  const size_t lds = 2 * Geo<D>::STAGEB;
+  const size_t lds = 4 * Geo<D>::TILEB;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)varlen_kernel<D>,
