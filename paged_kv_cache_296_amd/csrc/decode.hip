@@ -51,7 +51,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 2;        // waves per workgroup (independent units)
+constexpr int kWaves = 4;        // waves per workgroup (units of neighbouring kv heads)
 constexpr int kMaxSlice = 256;   // table entries one partition may span
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u;
 
@@ -571,11 +571,22 @@ void decode_partial_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int per_item = a.num_kv_heads * a.head_chunks;
   const unsigned total = (unsigned)a.ctrl[1] * (unsigned)per_item;
-  int ticket = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
-  for (;;) {
-    const unsigned u = (unsigned)__builtin_amdgcn_readfirstlane(ticket);
-    if (u >= total) break;
-    ticket = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
+  // Tickets are taken per workgroup: ticket T is units kWaves T .. kWaves T +
+  // kWaves-1, one per wave -- neighbouring kv heads of the same run, whose
+  // rows sit side by side in every block, so the workgroup's loads of a
+  // tile land on one contiguous kWaves x head-row span of the block.  Wave 0
+  // takes the tickets and passes them on through LDS (double buffered by
+  // iteration parity, one barrier per unit).
+  __shared__ unsigned s_ticket[2];
+  int ticket = (wave == 0 && lane == 0) ? atomicAdd(&a.ctrl[0], 1) : 0;
+  for (int it = 0;; ++it) {
+    if (wave == 0) s_ticket[it & 1] = (unsigned)__builtin_amdgcn_readfirstlane(ticket);
+    __syncthreads();
+    const unsigned T = (unsigned)__builtin_amdgcn_readfirstlane(s_ticket[it & 1]);
+    if ((unsigned long long)T * kWaves >= total) break;
+    if (wave == 0 && lane == 0) ticket = atomicAdd(&a.ctrl[0], 1);
+    const unsigned u = T * kWaves + wave;
+    if (u >= total) continue;
     const int4 item = a.items[u / (unsigned)per_item];
     const int r = (int)(u % (unsigned)per_item);
     const int packed = __builtin_amdgcn_readfirstlane(item.y);
