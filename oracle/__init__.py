@@ -60,6 +60,11 @@ def lib():
         L.pkvo_merge2.restype = None
         L.pkvo_finalize.argtypes = [D, P, I, P]
         L.pkvo_finalize.restype = None
+        L.pkvo_cache_write.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I]
+        L.pkvo_cache_write.restype = I
+        L.pkvo_varlen_paged.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, D, P,
+                                        I, P, I]
+        L.pkvo_varlen_paged.restype = I
         L.pkvo_max_threads.argtypes = []
         L.pkvo_max_threads.restype = I
         _lib = L
@@ -146,6 +151,60 @@ def varlen(q, k, v, cu_seq_lens_q, cu_seq_lens_k, max_length_q, max_length_k,
     rc = lib().pkvo_varlen(dt, _ptr(q3), _ptr(k3), _ptr(v3), _ptr(cq), _ptr(ck),
                            int(max_length_q), int(max_length_k), batch, total_q, total_k,
                            Hq, Hkv, D, float(scale), _ptr(rr), n_eval, _ptr(out), int(n_threads))
+    if rc:
+        raise OracleError(rc)
+    return out
+
+
+def cache_write(k, v, cu_seq_lens, start, k_cache, v_cache, block_table):
+    """Writes packed rows into the paged pools IN PLACE (pass copies you own).
+
+    k, v [1, total, Hkv, D] or [total, Hkv, D]; row cu[b] + i of request b goes
+    to token start[b] + i of sequence b.  Raises OracleError (pools untouched)
+    when any row cannot be placed.
+    """
+    dt = _dtype_code(k)
+    k3, v3 = _c(k.reshape(k.shape[-3:])), _c(v.reshape(v.shape[-3:]))
+    for a in (k_cache, v_cache):
+        if not (a.flags.c_contiguous and a.flags.writeable) or a.dtype != k.dtype:
+            raise ValueError("k_cache/v_cache must be writable C-contiguous arrays of k's dtype")
+    total, Hkv, D = k3.shape
+    num_blocks, bs, Hkv2, D2 = k_cache.shape
+    assert (Hkv2, D2) == (Hkv, D) and v_cache.shape == k_cache.shape
+    cu = _c(cu_seq_lens, np.int32)
+    st = _c(start, np.int32)
+    bt = _c(block_table, np.int32)
+    rc = lib().pkvo_cache_write(dt, _ptr(k3), _ptr(v3), _ptr(cu), _ptr(st), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(bt), len(cu) - 1, total, Hkv, D, num_blocks,
+                                bs, bt.shape[1])
+    if rc:
+        raise OracleError(rc)
+
+
+def varlen_paged(q, k_cache, v_cache, block_table, cu_seq_lens_q, seqlens_k, max_length_q,
+                 max_length_k, scale=None, rows=None, n_threads=0):
+    """Varlen attention (no mask) whose keys are the first seqlens_k[b] tokens
+    of sequence b in the paged pools, in fp64.
+
+    q [1, total_q, Hq, D] or [total_q, Hq, D].  Returns out [n_eval, Hq, D].
+    """
+    dt = _dtype_code(q)
+    q3 = _c(q.reshape(q.shape[-3:]))
+    total_q, Hq, D = q3.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    cq = _c(cu_seq_lens_q, np.int32)
+    sk = _c(seqlens_k, np.int32)
+    bt = _c(block_table, np.int32)
+    kc, vc = _c(k_cache), _c(v_cache)
+    rr = _c(rows, np.int32) if rows is not None else None
+    n_eval = len(rr) if rr is not None else total_q
+    out = np.zeros((n_eval, Hq, D), dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rc = lib().pkvo_varlen_paged(dt, _ptr(q3), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cq), _ptr(sk),
+                                 int(max_length_q), int(max_length_k), len(cq) - 1, total_q, Hq,
+                                 Hkv, D, num_blocks, bs, bt.shape[1], float(scale), _ptr(rr),
+                                 n_eval, _ptr(out), int(n_threads))
     if rc:
         raise OracleError(rc)
     return out

@@ -28,7 +28,9 @@
  *    entry, cache_seqlens holds each sequence's cached length, one query
  *    token per sequence, and the cache is updated in place.  Section "Jalur
  *    Varlen": packed sequences delimited by the cumulative lengths
- *    cu_seq_lens_q / cu_seq_lens_k, bounded by max_length_q / max_length_k.
+ *    cu_seq_lens_q / cu_seq_lens_k, bounded by max_length_q / max_length_k;
+ *    its cache-behaviour note: that kernel cannot reach the paged cache, so
+ *    the cache is written (and read) around it by a separate update.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - cache_seqlens counts tokens cached BEFORE the call; when new K/V are
@@ -372,6 +374,123 @@ int pkvo_varlen(int dtype, const void* q, const void* k, const void* v,
         for (int c = 0; c < D; ++c) o[c] += s[t] * widen(dtype, v, voff + c);
       }
       for (int c = 0; c < D; ++c) o[c] /= l;
+    }
+    free(s);
+  }
+  free(req);
+  return PKVO_OK;
+}
+
+/* -------------------------------------------------------- paged prefill */
+
+/*
+ * Writing packed rows into the paged cache.  The HF page, section "Jalur
+ * Varlen", cache behaviour: the varlen kernel cannot reach the paged cache,
+ * so new rows are written into it by a separate update.  Row cu[b] + i of
+ * request b is token start[b] + i of sequence b and goes to slot
+ * (block_table[b][p / bs], p mod bs), p = start[b] + i -- the same address
+ * rule as the decode append ("Jalur decode"), applied to every row.  A byte
+ * copy of the Hkv * D row, K and V alike.
+ *
+ *   k, v         [total, Hkv, D] dtype (the leading 1 is dropped)
+ *   cu           [batch+1] int32, start [batch] int32 (>= 0)
+ *   k_cache, v_cache [num_blocks, bs, Hkv, D], host copies, MUTATED
+ *
+ * Every row is located first; on any error nothing is written.
+ */
+int pkvo_cache_write(int dtype, const void* k, const void* v, const int32_t* cu,
+                     const int32_t* start, void* k_cache, void* v_cache,
+                     const int32_t* block_table, int batch, int total, int Hkv, int D,
+                     int num_blocks, int bs, int max_blocks_per_seq) {
+  if (batch < 0 || total < 0 || Hkv <= 0 || D <= 0 || bs <= 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || (dtype != PKVO_F32 && dtype != PKVO_BF16))
+    return PKVO_ERR_ARGS;
+  if (cu[0] != 0 || cu[batch] != total) return PKVO_ERR_CU;
+  for (int b = 0; b < batch; ++b) {
+    if (cu[b + 1] < cu[b]) return PKVO_ERR_CU;
+    if (start[b] < 0) return PKVO_ERR_SEQLEN;
+    for (int i = 0; i < cu[b + 1] - cu[b]; ++i) {
+      int32_t w[3];
+      const int rc = pkvo_locate(block_table, max_blocks_per_seq, num_blocks, bs, b,
+                                 start[b] + i, w);
+      if (rc) return rc;
+    }
+  }
+  const size_t row_bytes = (size_t)Hkv * D * elem_size(dtype);
+  for (int b = 0; b < batch; ++b)
+    for (int i = 0; i < cu[b + 1] - cu[b]; ++i) {
+      int32_t w[3];
+      pkvo_locate(block_table, max_blocks_per_seq, num_blocks, bs, b, start[b] + i, w);
+      const int64_t slot = (int64_t)w[2] * bs + w[1];
+      const int64_t r = cu[b] + i;
+      memcpy((char*)k_cache + slot * row_bytes, (const char*)k + r * row_bytes, row_bytes);
+      memcpy((char*)v_cache + slot * row_bytes, (const char*)v + r * row_bytes, row_bytes);
+    }
+  return PKVO_OK;
+}
+
+/*
+ * Varlen attention whose keys come from the paged cache: query rows
+ * cu_q[b] .. cu_q[b+1]-1 of request b attend the first seqlens_k[b] tokens
+ * of sequence b, read through its block-table row, no mask.  This is the
+ * "Jalur Varlen" computation with the key rows found by the "Jalur decode"
+ * address rule; each (row, head) is the three-step recipe of inference-notes
+ * section 2, exactly as for a decode query.
+ *
+ *   q            [total_q, Hq, D] dtype
+ *   k_cache, v_cache [num_blocks, bs, Hkv, D]
+ *   block_table  [batch, max_blocks_per_seq] int32
+ *   cu_q [batch+1], seqlens_k [batch] int32
+ *   rows         q rows whose output is wanted (NULL = all)
+ *   out          [n_eval, Hq, D] fp64
+ */
+int pkvo_varlen_paged(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* cu_q, const int32_t* seqlens_k,
+                      int max_len_q, int max_len_k, int batch, int total_q, int Hq, int Hkv,
+                      int D, int num_blocks, int bs, int max_blocks_per_seq, double scale,
+                      const int32_t* rows, int n_rows, double* out, int n_threads) {
+  if (batch < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || Hq % Hkv != 0 || (dtype != PKVO_F32 && dtype != PKVO_BF16))
+    return PKVO_ERR_ARGS;
+  if (cu_q[0] != 0 || cu_q[batch] != total_q) return PKVO_ERR_CU;
+  for (int b = 0; b < batch; ++b) {
+    const int lq = cu_q[b + 1] - cu_q[b], lk = seqlens_k[b];
+    if (lq < 0) return PKVO_ERR_CU;
+    if (lk < 0) return PKVO_ERR_SEQLEN;
+    if (lq > max_len_q || lk > max_len_k) return PKVO_ERR_MAXLEN;
+    const int nblk = (lk + bs - 1) / bs;
+    if (nblk > max_blocks_per_seq) return PKVO_ERR_TABLE_SPAN;
+    for (int j = 0; j < nblk; ++j) {
+      const int32_t pb = block_table[(int64_t)b * max_blocks_per_seq + j];
+      if (pb < 0 || pb >= num_blocks) return PKVO_ERR_BLOCK;
+    }
+  }
+  const int n_eval = rows ? n_rows : total_q;
+  for (int e = 0; e < n_eval; ++e)
+    if (rows && (rows[e] < 0 || rows[e] >= total_q)) return PKVO_ERR_ARGS;
+  int32_t* req = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total_q > 0 ? total_q : 1));
+  int rc = pkvo_request_index(cu_q, batch, total_q, req);
+  if (rc) {
+    free(req);
+    return rc;
+  }
+  const int G = Hq / Hkv;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#endif
+  const int64_t units = (int64_t)n_eval * Hq;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_len_k > 0 ? max_len_k : 1));
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t uidx = 0; uidx < units; ++uidx) {
+      const int e = (int)(uidx / Hq), h = (int)(uidx % Hq);
+      const int r = rows ? rows[e] : e;
+      const int b = req[r];
+      /* q row r is addressed as "sequence" r of a [total_q, 1, Hq, D] batch */
+      decode_one(dtype, q, k_cache, v_cache, block_table + (int64_t)b * max_blocks_per_seq,
+                 seqlens_k[b], r, h, G, Hq, Hkv, D, bs, scale, s,
+                 out + ((int64_t)e * Hq + h) * D);
     }
     free(s);
   }
