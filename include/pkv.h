@@ -20,6 +20,17 @@
  *               section "Jalur Varlen" (cu_seq_lens_q/k, max_length_q/k,
  *               packed shapes [1, total, heads, head_dim]).
  *
+ * Two more calls serve a prefill over a paged cache.  The same "Jalur
+ * Varlen" section notes that the varlen kernel cannot reach the paged cache,
+ * so the cache must be written (and read) around it by a separate update:
+ *
+ *   pkv_cache_write   scatters packed new K/V rows into their cache slots
+ *                     through the block table (the "Jalur decode" address
+ *                     rule applied to every row), bit for bit.
+ *   pkv_varlen_paged  the varlen computation with each request's keys read
+ *                     straight from the paged cache through its block-table
+ *                     row, so no packed copy of a cached prefix is needed.
+ *
  * Conventions shared by every call
  *  - Every tensor pointer is DEVICE memory owned by the caller, row-major,
  *    densely packed in the shape given.  The library allocates nothing,
@@ -205,6 +216,83 @@ int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
                int max_length_q, int max_length_k, void* out,
                int batch, int total_q, int total_k, int num_heads, int num_kv_heads,
                int head_dim, float softmax_scale, int32_t* err_flag, void* stream);
+
+/*
+ * Host-only validation of pkv_cache_write's scalar arguments.  Supported:
+ * fp32 or bf16; head_dim 64 or 128; block_size 16 or 32.
+ */
+int pkv_check_cache_write_args(int dtype, int batch, int total, int num_kv_heads, int head_dim,
+                               int num_blocks, int block_size, int max_blocks_per_seq);
+
+/*
+ * Writes packed K/V rows into the paged cache (HF page, "Jalur Varlen",
+ * cache behaviour; slot rule of "Jalur decode").
+ *
+ *   k, v           [1, total, num_kv_heads, head_dim]: new rows, request b's
+ *                    rows are cu_seq_lens[b] .. cu_seq_lens[b+1]-1.
+ *   cu_seq_lens    [batch + 1] int32 (cu[0] = 0, non-decreasing, cu[batch] =
+ *                    total).
+ *   start          [batch] int32: tokens of sequence b already cached; row
+ *                    cu[b] + i becomes token p = start[b] + i, stored at slot
+ *                    p mod block_size of physical block block_table[b][p /
+ *                    block_size].  Never modified (the caller advances it).
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim]; only
+ *                    the target slots are written, each with a bit-for-bit
+ *                    copy of its row.
+ *   block_table    [batch, max_blocks_per_seq] int32; the caller has put every
+ *                    needed block in the table.
+ *   err_flag       device int32, optional.
+ *
+ * A row whose slot cannot be resolved (cu not a valid cumulative array:
+ * PKV_ERR_CU; start < 0 or p past the table row: PKV_ERR_SPAN; entry -1 or
+ * >= num_blocks: PKV_ERR_BLOCK) is not written and sets the bit; the other
+ * rows are written.  Two rows must not target the same slot.
+ */
+int pkv_cache_write(int dtype, const void* k, const void* v, const int32_t* cu_seq_lens,
+                    const int32_t* start, void* k_cache, void* v_cache,
+                    const int32_t* block_table, int batch, int total, int num_kv_heads,
+                    int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+                    int32_t* err_flag, void* stream);
+
+/*
+ * Host-only validation of pkv_varlen_paged's scalar arguments.  Supported:
+ * bf16; head_dim 64 or 128; block_size 16 or 32; num_heads a multiple of
+ * num_kv_heads; max_length_k at most 2048 table entries (32768 tokens at
+ * block_size 16).
+ */
+int pkv_check_varlen_paged_args(int dtype, int batch, int total_q, int num_heads,
+                                int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                                int max_blocks_per_seq, int max_length_q, int max_length_k);
+
+/*
+ * Varlen attention (no mask) whose keys come from the paged cache: query rows
+ * cu_seq_lens_q[b] .. cu_seq_lens_q[b+1]-1 attend the first seqlens_k[b]
+ * tokens of sequence b, read through block_table[b] (HF page "Jalur Varlen"
+ * computation, "Jalur decode" addressing).
+ *
+ *   q              [1, total_q, num_heads, head_dim]
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim]; read only.
+ *   block_table    [batch, max_blocks_per_seq] int32; entries j <
+ *                    ceil(seqlens_k[b] / block_size) are read.
+ *   cu_seq_lens_q  [batch + 1] int32.
+ *   seqlens_k      [batch] int32: keys of request b (0 gives zeros).
+ *   max_length_q,  upper bounds on the per-request lengths; they size the
+ *   max_length_k     launch.  A longer request is a data error.
+ *   out            [1, total_q, num_heads, head_dim].
+ *   err_flag       device int32, optional: PKV_ERR_CU, PKV_ERR_MAXLEN,
+ *                    PKV_ERR_SPAN (seqlens_k < 0 or past the table row),
+ *                    PKV_ERR_BLOCK; the request's rows get NaN.
+ *
+ * Given the same keys, the output equals pkv_varlen's bit for bit: the
+ * kernels share their arithmetic and differ only in where a key tile is
+ * fetched from.
+ */
+int pkv_varlen_paged(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* cu_seq_lens_q,
+                     const int32_t* seqlens_k, int max_length_q, int max_length_k, void* out,
+                     int batch, int total_q, int num_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int block_size, int max_blocks_per_seq,
+                     float softmax_scale, int32_t* err_flag, void* stream);
 
 #ifdef __cplusplus
 }

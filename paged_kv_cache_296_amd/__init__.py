@@ -17,9 +17,10 @@ import os
 import torch
 
 __all__ = [
-    "PkvError", "decode", "decode_partials", "decode_merge", "varlen", "decode_workspace_bytes", "decode_partition_tokens",
-    "check_decode_args", "check_varlen_args", "status_string", "abi_version", "lib_path",
-    "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
+    "PkvError", "decode", "decode_partials", "decode_merge", "varlen", "cache_write",
+    "varlen_paged", "decode_workspace_bytes", "decode_partition_tokens", "check_decode_args",
+    "check_varlen_args", "check_cache_write_args", "check_varlen_paged_args", "status_string",
+    "abi_version", "lib_path", "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
@@ -64,6 +65,15 @@ def _load():
         L.pkv_check_varlen_args.restype = I
         L.pkv_varlen.argtypes = [I, P, P, P, P, P, I, I, P, I, I, I, I, I, I, F, P, P]
         L.pkv_varlen.restype = I
+        L.pkv_check_cache_write_args.argtypes = [I] * 8
+        L.pkv_check_cache_write_args.restype = I
+        L.pkv_cache_write.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+        L.pkv_cache_write.restype = I
+        L.pkv_check_varlen_paged_args.argtypes = [I] * 11
+        L.pkv_check_varlen_paged_args.restype = I
+        L.pkv_varlen_paged.argtypes = [I, P, P, P, P, P, P, I, I, P, I, I, I, I, I, I, I, I, F,
+                                       P, P]
+        L.pkv_varlen_paged.restype = I
         _lib = L
     return _lib
 
@@ -253,4 +263,106 @@ def varlen(q, k, v, cu_seq_lens_q, cu_seq_lens_k, max_length_q, max_length_k, *,
                         float(softmax_scale), _ptr(err_flag), _stream(stream))
     if rc:
         raise PkvError(rc, "pkv_varlen")
+    return out
+
+
+def check_cache_write_args(dtype, batch, total, num_kv_heads, head_dim, num_blocks, block_size,
+                           max_blocks_per_seq) -> int:
+    """Host-only validation (no GPU needed); returns a status code."""
+    return _load().pkv_check_cache_write_args(int(dtype), int(batch), int(total),
+                                              int(num_kv_heads), int(head_dim), int(num_blocks),
+                                              int(block_size), int(max_blocks_per_seq))
+
+
+def check_varlen_paged_args(dtype, batch, total_q, num_heads, num_kv_heads, head_dim, num_blocks,
+                            block_size, max_blocks_per_seq, max_length_q, max_length_k) -> int:
+    """Host-only validation (no GPU needed); returns a status code."""
+    return _load().pkv_check_varlen_paged_args(
+        int(dtype), int(batch), int(total_q), int(num_heads), int(num_kv_heads), int(head_dim),
+        int(num_blocks), int(block_size), int(max_blocks_per_seq), int(max_length_q),
+        int(max_length_k))
+
+
+def _cache_shape(k_cache, v_cache):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache/v_cache must both be [num_blocks, block_size, Hkv, D] of one dtype")
+    return k_cache.shape
+
+
+def cache_write(k, v, cu_seq_lens, start, k_cache, v_cache, block_table, *, err_flag=None,
+                stream=None):
+    """Writes packed rows into the paged cache in place.
+
+    k, v [1, total, Hkv, D]; row cu_seq_lens[b] + i becomes token start[b] + i
+    of sequence b (slot through block_table[b]).  Returns nothing; k_cache and
+    v_cache are updated on the stream.
+    """
+    lib = _load()
+    _need_gpu(k, v, cu_seq_lens, start, k_cache, v_cache, block_table, err_flag)
+    _need_contig(k=k, v=v, cu_seq_lens=cu_seq_lens, start=start, k_cache=k_cache,
+                 v_cache=v_cache, block_table=block_table)
+    dt = _dtype_code(k)
+    NB, bs, Hkv, D = _cache_shape(k_cache, v_cache)
+    if k.dim() != 4 or k.shape[0] != 1 or k.shape != v.shape or tuple(k.shape[2:]) != (Hkv, D):
+        raise ValueError("k, v must be [1, total, Hkv, D] matching the cache rows")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+        raise ValueError("k, v and the caches must share a dtype")
+    for name, t in (("cu_seq_lens", cu_seq_lens), ("start", start), ("block_table", block_table)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    B = start.shape[0]
+    if cu_seq_lens.dim() != 1 or cu_seq_lens.shape[0] != B + 1 or block_table.dim() != 2 or \
+            block_table.shape[0] != B:
+        raise ValueError("cu_seq_lens must be [batch + 1], start [batch], block_table [batch, max_blocks]")
+    total = k.shape[1]
+    rc = lib.pkv_cache_write(dt, _ptr(k), _ptr(v), _ptr(cu_seq_lens), _ptr(start),
+                             _ptr(k_cache), _ptr(v_cache), _ptr(block_table), B, total, Hkv, D,
+                             NB, bs, block_table.shape[1], _ptr(err_flag), _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_cache_write")
+
+
+def varlen_paged(q, k_cache, v_cache, block_table, cu_seq_lens_q, seqlens_k, max_length_q,
+                 max_length_k, *, softmax_scale=None, out=None, err_flag=None, stream=None):
+    """Varlen attention (no mask) with keys read through the block table.
+
+    q [1, total_q, Hq, D]; caches [num_blocks, block_size, Hkv, D];
+    block_table [batch, max_blocks] int32; cu_seq_lens_q [batch + 1] int32;
+    seqlens_k [batch] int32 (keys of request b = its first seqlens_k[b]
+    cached tokens).  Returns out [1, total_q, Hq, D] in q's dtype.
+    """
+    lib = _load()
+    _need_gpu(q, k_cache, v_cache, block_table, cu_seq_lens_q, seqlens_k, out, err_flag)
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                 cu_seq_lens_q=cu_seq_lens_q, seqlens_k=seqlens_k, out=out)
+    dt = _dtype_code(q)
+    NB, bs, Hkv, D = _cache_shape(k_cache, v_cache)
+    if q.dim() != 4 or q.shape[0] != 1 or q.shape[3] != D or k_cache.dtype != q.dtype:
+        raise ValueError("q must be [1, total_q, Hq, D] with the caches' head_dim and dtype")
+    for name, t in (("block_table", block_table), ("cu_seq_lens_q", cu_seq_lens_q),
+                    ("seqlens_k", seqlens_k)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    B = seqlens_k.shape[0]
+    if cu_seq_lens_q.dim() != 1 or cu_seq_lens_q.shape[0] != B + 1 or block_table.dim() != 2 or \
+            block_table.shape[0] != B:
+        raise ValueError("cu_seq_lens_q must be [batch + 1], seqlens_k [batch], block_table [batch, max_blocks]")
+    _, Tq, Hq, _ = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rc = lib.pkv_check_varlen_paged_args(dt, B, Tq, Hq, Hkv, D, NB, bs, block_table.shape[1],
+                                         int(max_length_q), int(max_length_k))
+    if rc:
+        raise PkvError(rc, "pkv_varlen_paged arguments")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    rc = lib.pkv_varlen_paged(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                              _ptr(cu_seq_lens_q), _ptr(seqlens_k), int(max_length_q),
+                              int(max_length_k), _ptr(out), B, Tq, Hq, Hkv, D, NB, bs,
+                              block_table.shape[1], float(softmax_scale), _ptr(err_flag),
+                              _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_varlen_paged")
     return out

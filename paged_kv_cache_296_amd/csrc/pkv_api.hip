@@ -12,7 +12,7 @@
 namespace {
 
 constexpr int kMaxPartitionBlocks = 256;  // LDS table slice per wave
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool decode_shape_ok(int head_dim, int block_size) {
   return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
@@ -259,7 +259,7 @@ int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
   const int rows = pkv::varlen_rows_per_workgroup(num_heads / num_kv_heads);
   const long long tiles = ((long long)max_length_q + rows - 1) / rows;
   if (tiles > 65535 || batch > 65535 || num_heads > 65535) return PKV_EUNSUPPORTED;
-  pkv::VarlenArgs a;
+  pkv::VarlenArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -279,6 +279,117 @@ int pkv_varlen(int dtype, const void* q, const void* k, const void* v,
   a.q_tiles = (int)tiles;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipError_t e = pkv::launch_varlen(dtype, head_dim, a, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+
+int pkv_check_cache_write_args(int dtype, int batch, int total, int num_kv_heads, int head_dim,
+                               int num_blocks, int block_size, int max_blocks_per_seq) {
+  if (batch < 0 || total < 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return PKV_EINVAL;
+  if (batch == 0 && total != 0) return PKV_EINVAL;
+  if (dtype != PKV_FP32 && dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PKV_EUNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT32_MAX) return PKV_EINVAL;
+  if ((long long)num_kv_heads * head_dim * (dtype == PKV_BF16 ? 2 : 4) > INT32_MAX / 2)
+    return PKV_EINVAL;
+  return PKV_OK;
+}
+
+int pkv_cache_write(int dtype, const void* k, const void* v, const int32_t* cu_seq_lens,
+                    const int32_t* start, void* k_cache, void* v_cache,
+                    const int32_t* block_table, int batch, int total, int num_kv_heads,
+                    int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+                    int32_t* err_flag, void* stream) {
+  int rc = pkv_check_cache_write_args(dtype, batch, total, num_kv_heads, head_dim, num_blocks,
+                                      block_size, max_blocks_per_seq);
+  if (rc != PKV_OK) return rc;
+  if (batch == 0) return PKV_OK;
+  if (!cu_seq_lens || !start || !block_table || !k_cache || !v_cache ||
+      (total > 0 && (!k || !v)))
+    return PKV_EINVAL;
+  pkv::CacheWriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.cu = cu_seq_lens;
+  a.start = start;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.err_flag = err_flag;
+  a.batch = batch;
+  a.total = total;
+  a.row_bytes = num_kv_heads * head_dim * (dtype == PKV_BF16 ? 2 : 4);
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  hipError_t e = pkv::launch_cache_write(a, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int pkv_check_varlen_paged_args(int dtype, int batch, int total_q, int num_heads,
+                                int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                                int max_blocks_per_seq, int max_length_q, int max_length_k) {
+  if (batch < 0 || total_q < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || max_length_q < 0 || max_length_k < 0)
+    return PKV_EINVAL;
+  if (dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PKV_EUNSUPPORTED;
+  if ((long long)max_length_k > (long long)pkv::kVarlenMaxTableEntries * block_size)
+    return PKV_EUNSUPPORTED;
+  if ((long long)total_q * num_heads * head_dim * 2 > (1LL << 31) * 64) return PKV_EINVAL;
+  // a block's bytes per kv head row set must stay a 32-bit buffer range
+  if ((long long)block_size * num_kv_heads * head_dim * 2 > INT32_MAX) return PKV_EINVAL;
+  return PKV_OK;
+}
+
+int pkv_varlen_paged(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* cu_seq_lens_q,
+                     const int32_t* seqlens_k, int max_length_q, int max_length_k, void* out,
+                     int batch, int total_q, int num_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int block_size, int max_blocks_per_seq,
+                     float softmax_scale, int32_t* err_flag, void* stream) {
+  int rc = pkv_check_varlen_paged_args(dtype, batch, total_q, num_heads, num_kv_heads, head_dim,
+                                       num_blocks, block_size, max_blocks_per_seq, max_length_q,
+                                       max_length_k);
+  if (rc != PKV_OK) return rc;
+  if (!isfinite(softmax_scale)) return PKV_EINVAL;
+  if (batch == 0 || total_q == 0) return PKV_OK;
+  if (!q || !out || !cu_seq_lens_q || !seqlens_k || !block_table ||
+      (max_length_k > 0 && (!k_cache || !v_cache)))
+    return PKV_EINVAL;
+  const int group = num_heads / num_kv_heads;
+  const int rows = pkv::varlen_rows_per_workgroup(group);
+  const long long tiles = ((long long)max_length_q + rows - 1) / rows;
+  if (tiles > 65535 || batch > 65535 || num_heads > 65535) return PKV_EUNSUPPORTED;
+  pkv::VarlenArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.cu_q = cu_seq_lens_q;
+  a.cu_k = nullptr;
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.out = out;
+  a.err_flag = err_flag;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.total_k = 0;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_len_q = max_length_q;
+  a.max_len_k = max_length_k;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.heads_per_wg = pkv::varlen_heads_per_workgroup(group);
+  a.q_tiles = (int)tiles;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = pkv::launch_varlen_paged(dtype, head_dim, a, (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

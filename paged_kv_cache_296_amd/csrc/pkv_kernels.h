@@ -1,5 +1,6 @@
 // Internal interface between the host entry points (pkv_api.hip) and the
-// kernels (decode.hip, varlen.hip).  Not part of the public ABI.
+// kernels (decode.hip, varlen.hip, cache_write.hip).  Not part of the public
+// ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,19 +35,38 @@ struct DecodeArgs {
   long long total_units;  // upper bound: batch * n_parts * num_kv_heads * head_chunks
 };
 
+// Packed varlen (k, v packed, cu_k) or paged varlen (k, v are the caches,
+// keys through block_table, lengths seqlens_k).
 struct VarlenArgs {
   const void* q;
   const void* k;
   const void* v;
   const int32_t* cu_q;
-  const int32_t* cu_k;
+  const int32_t* cu_k;         // packed only
+  const int32_t* block_table;  // paged only: [batch, max_blocks_per_seq]
+  const int32_t* seqlens_k;    // paged only: [batch]
   void* out;
   int32_t* err_flag;
   int batch, total_q, total_k, num_heads, num_kv_heads, group;
   int max_len_q, max_len_k;
+  int num_blocks, block_size, max_blocks_per_seq;  // paged only
   int heads_per_wg;   // q heads of one kv group sharing a workgroup (1, 2 or 4)
   int q_tiles;        // ceil(max_len_q / rows per workgroup)
   float scale_log2;
+};
+
+struct CacheWriteArgs {
+  const void* k;
+  const void* v;
+  const int32_t* cu;
+  const int32_t* start;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  int32_t* err_flag;
+  int batch, total;
+  int row_bytes;      // num_kv_heads * head_dim * element size (a multiple of 16)
+  int num_blocks, block_size, max_blocks_per_seq;
 };
 
 // Launchers return hipSuccess or the launch error.  dtype: 0 fp32, 1 bf16.
@@ -54,6 +74,10 @@ struct VarlenArgs {
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
                          int phases, hipStream_t stream);
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
+hipError_t launch_varlen_paged(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+// Table entries one paged-varlen workgroup stages in LDS (bounds max_length_k).
+constexpr int kVarlenMaxTableEntries = 2048;
 // Workgroup shape of the varlen kernel for a q-heads-per-kv-head ratio.
 int varlen_heads_per_workgroup(int group);
 int varlen_rows_per_workgroup(int group);

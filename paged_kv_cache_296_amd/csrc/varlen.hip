@@ -55,7 +55,7 @@ constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kWaveRows = 32;    // query rows per wave
 constexpr int kKeys = 64;        // keys per LDS tile
 constexpr float kLazy = 8.f;     // log2 of the largest exponential kept before a rescale
-constexpr unsigned kErrCu = 4u, kErrMaxLen = 8u;
+constexpr unsigned kErrBlock = 1u, kErrSpan = 2u, kErrCu = 4u, kErrMaxLen = 8u;
 
 template <int D>
 struct Geo {
@@ -133,6 +133,34 @@ __device__ __forceinline__ void issue_tile(const char* g, long long t0, int vali
     int o = off[i];
     if (PARTIAL) o -= max(((wave * G::NLOAD + i) * 64 + lane) / G::CH - (valid - 1), 0) * tok;
     load_to_lds(rs, o, (u32)(uintptr_t)(tile + (wave * G::NLOAD + i) * 1024));
+  }
+}
+
+// Paged keys: tile rows t0 .. t0+63 of the request are tokens of the
+// table-listed blocks.  A wave's share of a tile (16 consecutive rows, 16 or
+// 32 per block, tiles starting on a 64-token boundary) lies in ONE block, so
+// the block id is one LDS read per wave and tile, and the buffer descriptor is
+// bounded to that block.  Rows past len_k are clamped to the last key (same
+// block: the clamp never leaves the wave's 16-row group unless every row of
+// the wave is clamped).  coff: the lane's swizzled chunk offset per load.
+template <int D, bool PARTIAL>
+__device__ __forceinline__ void issue_tile_paged(const char* cache, const int* slice, int t0,
+                                                 int len_k, int bs, int tok, lds_char* tile,
+                                                 int wave, int lane, const int* coff) {
+  using G = Geo<D>;
+  constexpr int RPI = 1024 / G::ROWB;     // rows per 1 KB load
+  constexpr int RPW = G::NLOAD * RPI;     // rows per wave per tile
+  const int tw = t0 + RPW * wave;
+  const int tf = PARTIAL ? min(tw, len_k - 1) : tw;
+  const int j = tf / bs;
+  const int pb = __builtin_amdgcn_readfirstlane(slice[j]);
+  const u32x4 rs = vsharp(cache + (long long)pb * bs * tok, bs * tok);
+#pragma unroll
+  for (int i = 0; i < G::NLOAD; ++i) {
+    int tl = tw + i * RPI + lane / G::CH;
+    if (PARTIAL) tl = min(tl, len_k - 1);
+    load_to_lds(rs, (tl - j * bs) * tok + coff[i],
+                (u32)(uintptr_t)(tile + (wave * G::NLOAD + i) * 1024));
   }
 }
 
@@ -272,7 +300,9 @@ __device__ __forceinline__ void pv(lds_char* vt, const int* voff, const u32 (&pw
   }
 }
 
-template <int D>
+// PAGED = false: keys packed like the queries (cu_k); true: keys are the
+// first seqlens_k[b] tokens of sequence b in the paged cache (block_table).
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void varlen_kernel(VarlenArgs a) {
   using G = Geo<D>;
@@ -287,15 +317,30 @@ void varlen_kernel(VarlenArgs a) {
   const int wg_rows = kWaveRows * rb;
 
   const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
-  const int k0s = a.cu_k[b], k1s = a.cu_k[b + 1];
-  const int len_q = q1 - q0, len_k = k1s - k0s;
-  const bool cu_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && k0s >= 0 && k1s >= k0s &&
-                     k1s <= a.total_k && (b != 0 || (q0 == 0 && k0s == 0)) &&
-                     (b != a.batch - 1 || (q1 == a.total_q && k1s == a.total_k));
-  const bool len_ok = len_q <= a.max_len_q && len_k <= a.max_len_k;
-  if (!cu_ok || !len_ok) {
-    if (a.err_flag && tid == 0 && qt == 0 && blockIdx.y == 0)
-      atomicOr(a.err_flag, (int)(cu_ok ? kErrMaxLen : kErrCu));
+  const int len_q = q1 - q0;
+  const bool q_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && (b != 0 || q0 == 0) &&
+                    (b != a.batch - 1 || q1 == a.total_q);
+  int k0s = 0, len_k;
+  unsigned err = 0;
+  if constexpr (PAGED) {
+    len_k = a.seqlens_k[b];
+    if (!q_ok) err = kErrCu;
+    else if (len_k < 0 || (long long)len_k > (long long)a.max_blocks_per_seq * a.block_size)
+      err = kErrSpan;
+    else if (len_q > a.max_len_q || len_k > a.max_len_k) err = kErrMaxLen;
+  } else {
+    k0s = a.cu_k[b];
+    const int k1s = a.cu_k[b + 1];
+    len_k = k1s - k0s;
+    const bool cu_ok = q_ok && k0s >= 0 && k1s >= k0s && k1s <= a.total_k &&
+                       (b != 0 || k0s == 0) && (b != a.batch - 1 || k1s == a.total_k);
+    if (!cu_ok) err = kErrCu;
+    else if (len_q > a.max_len_q || len_k > a.max_len_k) err = kErrMaxLen;
+  }
+  // A request the kernel cannot run: flag it and write NaN to its rows (when
+  // the rows themselves can be located).
+  auto fail = [&](unsigned bit) {
+    if (a.err_flag && tid == 0 && qt == 0 && blockIdx.y == 0) atomicOr(a.err_flag, (int)bit);
     if (!(q0 >= 0 && q1 >= q0 && q1 <= a.total_q)) return;  // nowhere safe to write
     const int r0 = qt * wg_rows, r1 = min(len_q, r0 + wg_rows);
     for (int i = tid; i < (r1 > r0 ? (r1 - r0) * hpw : 0); i += 256) {
@@ -303,6 +348,9 @@ void varlen_kernel(VarlenArgs a) {
       __bf16* o = (__bf16*)a.out + ((long long)(q0 + r) * a.num_heads + hq) * D;
       for (int d = 0; d < D; ++d) o[d] = (__bf16)__builtin_nanf("");
     }
+  };
+  if (err) {
+    fail(err);
     return;
   }
   if (qt * wg_rows >= len_q) return;
@@ -314,6 +362,23 @@ void varlen_kernel(VarlenArgs a) {
   const char* kg = (const char*)a.k + (long long)k0s * tok_k + (long long)kvh * D * 2;
   const char* vg = (const char*)a.v + (long long)k0s * tok_k + (long long)kvh * D * 2;
   lds_char* lds = (lds_char*)smem;
+  // paged: the request's table entries, validated and staged in LDS after
+  // the four tiles
+  int* slice = reinterpret_cast<int*>(smem + 4 * G::TILEB);
+  if constexpr (PAGED) {
+    const int nblk = (len_k + a.block_size - 1) / a.block_size;
+    const int32_t* trow = a.block_table + (long long)b * a.max_blocks_per_seq;
+    bool bad = false;
+    for (int e = tid; e < nblk; e += 256) {
+      const int pb = trow[e];
+      bad |= pb < 0 || pb >= a.num_blocks;
+      slice[e] = pb;
+    }
+    if (__syncthreads_or(bad)) {
+      fail(kErrBlock);
+      return;
+    }
+  }
 
   // this lane's query row as the B operand: dims 16 s + 8 hh + 0..7; a
   // negative scale is folded into q (a sign flip is exact in bf16)
@@ -335,12 +400,14 @@ void varlen_kernel(VarlenArgs a) {
   }
 
   // lane offsets: tile loads (same for K and V), K operand reads, V^T reads
+  // (packed: row offset + swizzled chunk; paged: the swizzled chunk only, the
+  // row offset depends on the block)
   int loff[G::NLOAD];
 #pragma unroll
   for (int i = 0; i < G::NLOAD; ++i) {
     const int cl = (wave * G::NLOAD + i) * 64 + lane;
     const int r = cl / G::CH, ps = cl % G::CH;
-    loff[i] = r * tok_k + 16 * (ps ^ swz<D>(r));
+    loff[i] = (PAGED ? 0 : r * tok_k) + 16 * (ps ^ swz<D>(r));
   }
   int koff[G::KS];
 #pragma unroll
@@ -375,10 +442,19 @@ void varlen_kernel(VarlenArgs a) {
   auto kbuf = [&](int j) { return lds + (j & 1) * G::TILEB; };
   auto vbuf = [&](int j) { return lds + (2 + (j & 1)) * G::TILEB; };
   auto issue = [&](const char* g, int j, lds_char* tile) {
-    if (j + 1 < nk || !partial)
-      issue_tile<D, false>(g, (long long)j * kKeys, kKeys, tok_k, tile, wave, lane, loff);
-    else
-      issue_tile<D, true>(g, (long long)j * kKeys, last_valid, tok_k, tile, wave, lane, loff);
+    if constexpr (PAGED) {
+      if (j + 1 < nk || !partial)
+        issue_tile_paged<D, false>(g, slice, j * kKeys, len_k, a.block_size, tok_k, tile, wave,
+                                   lane, loff);
+      else
+        issue_tile_paged<D, true>(g, slice, j * kKeys, len_k, a.block_size, tok_k, tile, wave,
+                                  lane, loff);
+    } else {
+      if (j + 1 < nk || !partial)
+        issue_tile<D, false>(g, (long long)j * kKeys, kKeys, tok_k, tile, wave, lane, loff);
+      else
+        issue_tile<D, true>(g, (long long)j * kKeys, last_valid, tok_k, tile, wave, lane, loff);
+    }
   };
   auto wait_all = [&]() {
     // own loads done, then everyone's; this also retires every wave's reads
@@ -447,18 +523,19 @@ void varlen_kernel(VarlenArgs a) {
     }
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
-  const size_t lds = 4 * Geo<D>::TILEB;
+  const size_t lds = 4 * Geo<D>::TILEB + (PAGED ? kVarlenMaxTableEntries * sizeof(int) : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)varlen_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)varlen_kernel<D, PAGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(varlen_kernel<D>, dim3(a.q_tiles, a.num_heads / a.heads_per_wg, a.batch),
-                     dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((varlen_kernel<D, PAGED>),
+                     dim3(a.q_tiles, a.num_heads / a.heads_per_wg, a.batch), dim3(256), lds,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -475,8 +552,18 @@ int varlen_rows_per_workgroup(int group) {
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream) {
   if (dtype != 1) return hipErrorInvalidValue;
   if (a.q_tiles == 0 || a.batch == 0) return hipSuccess;
-  if (head_dim == 128) return launch_v<128>(a, stream);
-  if (head_dim == 64) return launch_v<64>(a, stream);
+  if (head_dim == 128) return launch_v<128, false>(a, stream);
+  if (head_dim == 64) return launch_v<64, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_varlen_paged(int dtype, int head_dim, const VarlenArgs& a,
+                               hipStream_t stream) {
+  if (dtype != 1) return hipErrorInvalidValue;
+  if (a.q_tiles == 0 || a.batch == 0) return hipSuccess;
+  if (a.block_size % 16 != 0) return hipErrorInvalidValue;  // a wave's 16 rows in one block
+  if (head_dim == 128) return launch_v<128, true>(a, stream);
+  if (head_dim == 64) return launch_v<64, true>(a, stream);
   return hipErrorInvalidValue;
 }
 

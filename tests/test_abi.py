@@ -27,7 +27,9 @@ def pkv():
 def test_header_declares_the_calls():
     names = declared_functions()
     for must in ("pkv_decode", "pkv_varlen", "pkv_decode_workspace_bytes",
-                 "pkv_check_decode_args", "pkv_check_varlen_args", "pkv_status_string"):
+                 "pkv_check_decode_args", "pkv_check_varlen_args", "pkv_status_string",
+                 "pkv_cache_write", "pkv_varlen_paged", "pkv_check_cache_write_args",
+                 "pkv_check_varlen_paged_args"):
         assert must in names
 
 
@@ -74,6 +76,35 @@ def test_check_varlen_args(pkv, args, want):
     assert pkv.check_varlen_args(*args) == want
 
 
+@pytest.mark.parametrize("args,want", [
+    # dtype, batch, total, Hkv, D, num_blocks, bs, max_blocks
+    ((1, 16, 16000, 8, 128, 2634, 16, 241), 0),
+    ((0, 3, 3, 4, 64, 8, 32, 4), 0),              # fp32 rows are fine (a byte copy)
+    ((1, 0, 0, 8, 128, 10, 16, 4), 0),            # nothing to write
+    ((1, 0, 5, 8, 128, 10, 16, 4), 1),            # rows without a request
+    ((1, 4, 10, 8, 96, 10, 16, 4), 2),            # head_dim 96
+    ((1, 4, 10, 8, 128, 10, 8, 4), 2),            # block_size 8
+    ((1, 4, -1, 8, 128, 10, 16, 4), 1),
+    ((3, 4, 10, 8, 128, 10, 16, 4), 2),
+])
+def test_check_cache_write_args(pkv, args, want):
+    assert pkv.check_cache_write_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    # dtype, batch, total_q, Hq, Hkv, D, num_blocks, bs, max_blocks, max_q, max_k
+    ((1, 16, 16000, 32, 8, 128, 2634, 16, 241, 2048, 3848), 0),
+    ((1, 1, 1, 8, 8, 64, 10, 32, 4, 1, 2048 * 32), 0),      # the most keys the LDS table holds
+    ((1, 1, 1, 8, 8, 64, 10, 32, 4, 1, 2048 * 32 + 1), 2),
+    ((0, 16, 100, 32, 8, 128, 50, 16, 8, 60, 60), 2),        # bf16 only
+    ((1, 16, 100, 30, 8, 128, 50, 16, 8, 60, 60), 1),
+    ((1, 16, 100, 32, 8, 128, 50, 8, 8, 60, 60), 2),         # block_size 8
+    ((1, 16, 100, 32, 8, 80, 50, 16, 8, 60, 60), 2),
+])
+def test_check_varlen_paged_args(pkv, args, want):
+    assert pkv.check_varlen_paged_args(*args) == want
+
+
 def test_partition_plan_and_workspace(pkv):
     # explicit partition: 512 tokens over a 2048-block row -> 64 partitions
     assert pkv.decode_partition_tokens(256, 64, 8, 128, 16, 2048, 512) == 512
@@ -104,3 +135,8 @@ def test_product_path_refuses_cpu_tensors(pkv):
     with pytest.raises(ValueError, match="GPU"):
         pkv.varlen(torch.zeros(1, 4, 4, 64), torch.zeros(1, 4, 4, 64), torch.zeros(1, 4, 4, 64),
                    torch.tensor([0, 4], dtype=torch.int32), torch.tensor([0, 4], dtype=torch.int32), 4, 4)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.cache_write(torch.zeros(1, 4, 4, 64), torch.zeros(1, 4, 4, 64), cu, sl, kc, kc.clone(), bt)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.varlen_paged(torch.zeros(1, 4, 4, 64), kc, kc.clone(), bt, cu, sl, 4, 4)

@@ -222,6 +222,70 @@ def make_varlen(*, seed, dtype, batch, num_heads, num_kv_heads, head_dim, q_leng
                       softmax_scale=softmax_scale, q_lengths=lq, k_lengths=lk, seed=seed)
 
 
+@dataclass
+class PagedPrefillCase:
+    """A prefill step over a paged cache: request b has prefix[b] tokens
+    cached already and q_lengths[b] new tokens whose K/V rows (packed) are to
+    be written after them; its queries attend prefix + new keys."""
+    q: torch.Tensor             # [1, total_new, Hq, D]
+    k_new: torch.Tensor         # [1, total_new, Hkv, D] packed new rows
+    v_new: torch.Tensor
+    k_cache: torch.Tensor       # [num_blocks, block_size, Hkv, D] (prefix slots filled)
+    v_cache: torch.Tensor
+    block_table: torch.Tensor   # [batch, max_blocks] int32, covers prefix + new
+    cu_seq_lens_q: torch.Tensor  # [batch + 1] int32 (also the new rows' cu)
+    start: torch.Tensor         # [batch] int32 = prefix
+    seqlens_k: torch.Tensor     # [batch] int32 = prefix + new
+    max_length_q: int
+    max_length_k: int
+    softmax_scale: float
+    q_lengths: np.ndarray
+    prefix: np.ndarray
+    seed: int = 0
+
+
+def make_paged_prefill(*, seed, dtype, batch, num_heads, num_kv_heads, head_dim, q_lengths,
+                       prefix, block_size=16, num_blocks="total+5%", device="cpu",
+                       softmax_scale=None, **_):
+    """Same lengths as make_varlen with the same seed (len_k = len_q +
+    prefix), laid out in a paged pool: each sequence's prefix + new tokens get
+    blocks from a seeded permutation of the pool; the pool (prefix included)
+    is N(0,1)."""
+    rng = np.random.default_rng(seed)
+    lq = draw_lengths(rng, q_lengths, batch)
+    pre = draw_lengths(rng, prefix, batch)
+    tot = lq + pre
+    bs = block_size
+    need = np.ceil(tot / bs).astype(np.int64)
+    if num_blocks == "total+5%":
+        num_blocks = int(math.ceil(1.05 * int(need.sum()))) + 1
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    mb = max(1, int(need.max()) if batch else 1)
+    bt = np.full((batch, mb), -1, dtype=np.int32)
+    pos = 0
+    for i in range(batch):
+        n = int(need[i])
+        bt[i, :n] = perm[pos:pos + n]
+        pos += n
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    tdt = _tdtype(dtype)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    q = _randn((1, int(cq[-1]), num_heads, head_dim), gen, device, tdt)
+    kn = _randn((1, int(cq[-1]), num_kv_heads, head_dim), gen, device, tdt)
+    vn = _randn((1, int(cq[-1]), num_kv_heads, head_dim), gen, device, tdt)
+    kc = _randn((num_blocks, bs, num_kv_heads, head_dim), gen, device, tdt)
+    vc = _randn((num_blocks, bs, num_kv_heads, head_dim), gen, device, tdt)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    i32 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).to(device)
+    return PagedPrefillCase(q=q, k_new=kn, v_new=vn, k_cache=kc, v_cache=vc, block_table=i32(bt),
+                            cu_seq_lens_q=i32(cq), start=i32(pre), seqlens_k=i32(tot),
+                            max_length_q=int(lq.max()) if batch else 0,
+                            max_length_k=int(tot.max()) if batch else 0,
+                            softmax_scale=softmax_scale, q_lengths=lq, prefix=pre, seed=seed)
+
+
 def make_config(name: str, device="cpu", part=None):
     """The named workload: a DecodeCase, a VarlenCase, or for the mixed step
     (decode, varlen) -- or just one of them with part="decode"/"prefill"."""
