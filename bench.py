@@ -135,6 +135,69 @@ def time_varlen(pkv, torch, case, steps, warmup):
     return wall_ms, kern
 
 
+def time_call(torch, fn, steps, warmup, flush=None):
+    """Mean HIP-event time (ms) of fn() on the current stream.  With `flush`
+    (a byte tensor larger than the 256 MB last-level cache) it is
+    overwritten before every timed call, outside the timed interval, so that
+    fn() starts from a cold cache."""
+    for _ in range(warmup):
+        fn()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        evs[i][0].record()
+        fn()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+
+
+def paged_prefill_leg(pkv, torch, workloads, steps, warmup, dev):
+    """The prefill batch as a paged step: the new rows are written into their
+    cache slots (pkv_cache_write), then the queries attend prefix + new keys
+    straight from the paged pool (pkv_varlen_paged)."""
+    c = dict(workloads.CONFIGS["varlen_prefill"])
+    c.pop("kind")
+    pc = workloads.make_paged_prefill(device=dev, **c)
+    total, Hkv, D = pc.k_new.shape[1:]
+    row_bytes = Hkv * D * pc.k_new.element_size()
+    write_bytes = 4 * total * row_bytes         # K and V rows, read once and written once
+    fl = int(sum(4 * D * pc.q.shape[2] * int(a) * int(b)
+                 for a, b in zip(pc.q_lengths, pc.q_lengths + pc.prefix)))
+    out = torch.empty_like(pc.q)
+
+    def write():
+        pkv.cache_write(pc.k_new, pc.v_new, pc.cu_seq_lens_q, pc.start, pc.k_cache, pc.v_cache,
+                        pc.block_table)
+
+    def attend():
+        pkv.varlen_paged(pc.q, pc.k_cache, pc.v_cache, pc.block_table, pc.cu_seq_lens_q,
+                         pc.seqlens_k, pc.max_length_q, pc.max_length_k,
+                         softmax_scale=pc.softmax_scale, out=out)
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # reference: a plain device copy of the same rows (torch), same flush
+    kd, vd = torch.empty_like(pc.k_new), torch.empty_like(pc.v_new)
+    ck = time_call(torch, lambda: (kd.copy_(pc.k_new), vd.copy_(pc.v_new)), steps, warmup, flush)
+    del kd, vd
+    wk = time_call(torch, write, steps, warmup, flush)
+    ak = time_call(torch, attend, steps, warmup, flush)
+    sk = time_call(torch, lambda: (write(), attend()), steps, warmup, flush)
+    del flush
+    return {"workload": "paged_prefill (varlen_prefill lengths, 16-token blocks, permuted pool)",
+            "cache_write_ms": round(wk, 4), "cache_write_bytes": write_bytes,
+            "cache_write_gbs": round(write_bytes / (wk * 1e-3) / 1e9, 1),
+            "cache_write_frac_of_hbm_peak": round(write_bytes / (wk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "same_bytes_torch_copy_ms": round(ck, 4),
+            "same_bytes_torch_copy_gbs": round(write_bytes / (ck * 1e-3) / 1e9, 1),
+            "varlen_paged_ms": round(ak, 4), "flops": fl,
+            "varlen_paged_tflops": round(fl / (ak * 1e-3) / 1e12, 2),
+            "varlen_paged_frac_of_mfma_peak": round(fl / (ak * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "step_ms": round(sk, 4), "timing": "HIP events, last-level cache flushed before each call"}
+
+
 def cpu_baseline(torch, case, seconds):
     """The fp64 oracle on the host over a bounded, seeded sample of the
     workload's sequences (all heads), until about `seconds` of work."""
@@ -184,7 +247,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_b256_long",
                     choices=["decode_b256_long", "decode_b64_gqa4", "tiny_decode_fp32", "mixed_step",
-                             "varlen_prefill", "copy_1gib"])
+                             "varlen_prefill", "paged_prefill", "copy_1gib"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and mixed-step legs")
@@ -230,6 +293,11 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": None}}))
+        return
+
+    if args.workload == "paged_prefill":
+        r = paged_prefill_leg(pkv, torch, workloads, K, W, dev)
+        print(json.dumps(r))
         return
 
     log("generating", args.workload)
@@ -285,6 +353,12 @@ def main():
                           "frac_of_mfma_peak": round(fl / (pk * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         log("prefill", res["prefill"])
         del pcase
+        torch.cuda.empty_cache()
+        log("paged prefill leg")
+        res["paged_prefill"] = paged_prefill_leg(pkv, torch, workloads, max(K // 2, 5),
+                                                 max(W // 2, 2), dev)
+        log("paged prefill", res["paged_prefill"])
+        torch.cuda.empty_cache()
         log("mixed step leg: mixed_step")
         dcase, vcase = workloads.make_config("mixed_step", device=dev)
         dk = kv_bytes(dcase)

@@ -7,14 +7,15 @@
 // sequence b and is copied, bit for bit, to slot p mod block_size of
 // physical block block_table[b][p / block_size], for K and for V.
 //
-// How: one wave per packed row.  Everything that locates the row -- its
-// request (a binary search of cu), its token position, its table entry --
-// is wave-uniform, so it runs on the scalar unit from the scalar cache; the
-// 64 lanes then move the row's Hkv * D elements (2 KB per row of K at 8 kv
-// heads x 128 bf16) in 16-byte pieces, K and V interleaved so that each lane
-// has four loads in flight.  The row is contiguous at both ends (a token row
-// of the cache is [Hkv][D] like a packed row), so both sides are coalesced.
-// HBM bound: 2 reads + 2 writes of the row per packed row.
+// How: one wave per 4 consecutive packed rows.  Everything that locates a
+// row -- its request (one load of cu per lane and a ballot, or a binary
+// search for large batches), its token position, its table entry -- is
+// wave-uniform and runs on the scalar unit; the 64 lanes then move the rows'
+// Hkv * D elements (2 KB per row of K at 8 kv heads x 128 bf16) in 16-byte
+// pieces, issuing the loads of all 4 rows of K and V before any store, so
+// each lane has 16 loads in flight.  A row is contiguous at both ends (a
+// token row of the cache is [Hkv][D] like a packed row), so both sides are
+// coalesced.  HBM bound: 2 reads + 2 writes of the row per packed row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,7 +26,28 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWavesPerGroup = 4;
+constexpr int kRowsPerWave = 4;   // rows one wave copies, all loads in flight together
+constexpr int kMaxPieces = 4;     // 16-byte pieces per lane per row (row_bytes <= 4 KB)
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u, kErrCu = 4u;
+
+// The request of packed row r: the last b with cu[b] <= r.  Up to 63
+// requests: one load of cu per lane and a ballot; more: a binary search on
+// the scalar unit.
+__device__ __forceinline__ int request_of(const int32_t* cu, int batch, int r, int lane) {
+  if (batch < 64) {
+    const bool le = lane <= batch && cu[min(lane, batch)] <= r;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(le);
+    const int cnt = __builtin_popcountll(m);  // cu[0..cnt-1] <= r for a non-decreasing cu
+    return min(max(cnt - 1, 0), batch - 1);
+  }
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 
 __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheWriteArgs a) {
   const int lane = threadIdx.x & 63;
@@ -38,55 +60,76 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
     bad_cu |= a.cu[i + 1] < a.cu[i];
   if (gw == 0 && lane == 0) bad_cu |= a.cu[0] != 0 || a.cu[a.batch] != a.total;
   if (bad_cu && a.err_flag) atomicOr(a.err_flag, (int)kErrCu);
-  if (gw >= a.total || a.batch <= 0) return;
+  const long long r0 = gw * kRowsPerWave;
+  if (r0 >= a.total || a.batch <= 0) return;
 
-  // the request of row r: the last b with cu[b] <= r (uniform, scalar loads)
-  const int r = (int)gw;
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu[mid] <= r) lo = mid;
-    else hi = mid - 1;
-  }
-  const int b = lo;
-  const int c0 = a.cu[b], c1 = a.cu[b + 1];
-  unsigned err = 0;
-  if (!(c0 <= r && r < c1)) err = kErrCu;
-  const int st = a.start[b];
-  const long long p = (long long)st + (r - c0);
-  if (!err && (st < 0 || p >= (long long)a.max_blocks_per_seq * a.block_size)) err = kErrSpan;
-  int pb = 0;
-  if (!err) {
-    pb = a.block_table[(long long)b * a.max_blocks_per_seq + p / a.block_size];
-    if (pb < 0 || pb >= a.num_blocks) err = kErrBlock;
-  }
-  if (err) {
-    if (a.err_flag && lane == 0) atomicOr(a.err_flag, (int)err);
-    return;
-  }
-  const long long src = (long long)r * a.row_bytes;
-  const long long dst = ((long long)pb * a.block_size + p % a.block_size) * a.row_bytes;
-  const char* ks = (const char*)a.k + src;
-  const char* vs = (const char*)a.v + src;
-  char* kd = (char*)a.k_cache + dst;
-  char* vd = (char*)a.v_cache + dst;
+  // locate this wave's rows (uniform: scalar registers)
   const int n16 = a.row_bytes / 16;
-  int c = lane;
-  for (; c + 64 < n16; c += 128) {
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(ks + 16 * c);
-    const u32x4 k1 = *reinterpret_cast<const u32x4*>(ks + 16 * (c + 64));
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(vs + 16 * c);
-    const u32x4 v1 = *reinterpret_cast<const u32x4*>(vs + 16 * (c + 64));
-    *reinterpret_cast<u32x4*>(kd + 16 * c) = k0;
-    *reinterpret_cast<u32x4*>(kd + 16 * (c + 64)) = k1;
-    *reinterpret_cast<u32x4*>(vd + 16 * c) = v0;
-    *reinterpret_cast<u32x4*>(vd + 16 * (c + 64)) = v1;
+  const int nrows = (int)min((long long)kRowsPerWave, a.total - r0);
+  long long src[kRowsPerWave], dst[kRowsPerWave];
+  bool ok[kRowsPerWave];
+  int b = __builtin_amdgcn_readfirstlane(request_of(a.cu, a.batch, (int)r0, lane));
+  unsigned err = 0;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    ok[i] = false;
+    src[i] = dst[i] = 0;
+    if (i >= nrows) continue;
+    const int r = (int)r0 + i;
+    while (b + 1 < a.batch && a.cu[b + 1] <= r) ++b;  // rows are consecutive
+    const int c0 = a.cu[b], c1 = a.cu[b + 1];
+    if (!(c0 <= r && r < c1)) {
+      err |= kErrCu;
+      continue;
+    }
+    const int st = a.start[b];
+    const long long p = (long long)st + (r - c0);
+    if (st < 0 || p >= (long long)a.max_blocks_per_seq * a.block_size) {
+      err |= kErrSpan;
+      continue;
+    }
+    const int pb = a.block_table[(long long)b * a.max_blocks_per_seq + p / a.block_size];
+    if (pb < 0 || pb >= a.num_blocks) {
+      err |= kErrBlock;
+      continue;
+    }
+    ok[i] = true;
+    src[i] = (long long)r * a.row_bytes;
+    dst[i] = ((long long)pb * a.block_size + p % a.block_size) * a.row_bytes;
   }
-  if (c < n16) {
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(ks + 16 * c);
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(vs + 16 * c);
-    *reinterpret_cast<u32x4*>(kd + 16 * c) = k0;
-    *reinterpret_cast<u32x4*>(vd + 16 * c) = v0;
+  if (err && a.err_flag && lane == 0) atomicOr(a.err_flag, (int)err);
+
+  // all loads of the wave's rows first, then all stores
+  u32x4 kx[kRowsPerWave][kMaxPieces], vx[kRowsPerWave][kMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int c = lane + 64 * j;
+      if (ok[i] && c < n16) {
+        kx[i][j] = *reinterpret_cast<const u32x4*>((const char*)a.k + src[i] + 16 * c);
+        vx[i][j] = *reinterpret_cast<const u32x4*>((const char*)a.v + src[i] + 16 * c);
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int c = lane + 64 * j;
+      if (ok[i] && c < n16) {
+        *reinterpret_cast<u32x4*>((char*)a.k_cache + dst[i] + 16 * c) = kx[i][j];
+        *reinterpret_cast<u32x4*>((char*)a.v_cache + dst[i] + 16 * c) = vx[i][j];
+      }
+    }
+  // rows longer than 4 KB: the rest piece by piece
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    if (!ok[i]) continue;
+    for (int c = lane + 64 * kMaxPieces; c < n16; c += 64) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>((const char*)a.k + src[i] + 16 * c);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>((const char*)a.v + src[i] + 16 * c);
+      *reinterpret_cast<u32x4*>((char*)a.k_cache + dst[i] + 16 * c) = kv;
+      *reinterpret_cast<u32x4*>((char*)a.v_cache + dst[i] + 16 * c) = vv;
+    }
   }
 }
 
@@ -95,7 +138,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
   if (a.total == 0 && a.batch == 0) return hipSuccess;
   // at least one group so that cu is always checked
-  const long long groups = a.total > 0 ? (a.total + kWavesPerGroup - 1) / kWavesPerGroup : 1;
+  const long long per_group = (long long)kWavesPerGroup * kRowsPerWave;
+  const long long groups = a.total > 0 ? (a.total + per_group - 1) / per_group : 1;
   hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)groups), dim3(kWavesPerGroup * 64), 0,
                      stream, a);
   return hipGetLastError();

@@ -74,7 +74,8 @@ def test_cache_write_decode_example_slots(golden):
         assert torch.equal(kg[pb, g["cache_seqlens"][i] % 32], k[0, i])
 
 
-@pytest.mark.parametrize("D,Hkv,bs", [(64, 1, 16), (128, 8, 16), (128, 3, 32), (64, 5, 32)])
+@pytest.mark.parametrize("D,Hkv,bs", [(64, 1, 16), (128, 8, 16), (128, 3, 32), (64, 5, 32),
+                                     (128, 40, 16)])   # 10 KB rows: past the 4 KB fast path
 def test_cache_write_ragged(D, Hkv, bs):
     case = workloads.make_paged_prefill(seed=3300 + D + Hkv, dtype="bf16", batch=7, num_heads=Hkv,
                                         num_kv_heads=Hkv, head_dim=D,
