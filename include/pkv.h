@@ -67,7 +67,8 @@ typedef enum {
   PKV_EINVAL = 1,        /* null pointer, negative or inconsistent size      */
   PKV_EUNSUPPORTED = 2,  /* shape or dtype this build has no kernel for       */
   PKV_EWORKSPACE = 3,    /* workspace NULL or smaller than required           */
-  PKV_EHIP = 4           /* the HIP runtime refused a launch                  */
+  PKV_EHIP = 4,          /* the HIP runtime refused a launch                  */
+  PKV_ENOMEM = 5         /* block manager: not enough free blocks (nothing changed) */
 } pkv_status;
 
 typedef enum { PKV_FP32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -293,6 +294,92 @@ int pkv_varlen_paged(int dtype, const void* q, const void* k_cache, const void* 
                      int batch, int total_q, int num_heads, int num_kv_heads, int head_dim,
                      int num_blocks, int block_size, int max_blocks_per_seq,
                      float softmax_scale, int32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------ block manager
+ *
+ * Host-side bookkeeping of the physical blocks of one K/V pool (e2hang
+ * notes "Paged Attention", section "物理块管理" (physical block management,
+ * block allocation strategy), the logical-page mapping section before it,
+ * and its closing "注意事项" (block reclamation, shared-block reference
+ * counts); paweldubiel notes "PagedAttention", section "Mechanizm i
+ * szczegóły": blocks are added only as a sequence grows, unchanged blocks
+ * may be shared):
+ *  - a free list handed out from its end (pop) and refilled at its end
+ *    (push); initially blocks 0 .. num_blocks-1, so block num_blocks-1 goes
+ *    first;
+ *  - a sequence of L tokens owns ceil(L / block_size) blocks in logical
+ *    order; growing it by n tokens takes ceil((L+n) / block_size) minus the
+ *    blocks it has;
+ *  - too few free blocks is PKV_ENOMEM and changes nothing (no partial
+ *    allocation);
+ *  - blocks carry reference counts: a fork shares every block of the parent
+ *    with the child; a block returns to the free list when its count drops
+ *    to 0;
+ *  - copy-on-write: before an append writes into a partially filled last
+ *    block that another sequence also holds, that block is replaced in the
+ *    appending sequence by a fresh copy.  The manager only decides; the
+ *    caller copies the block contents on the GPU (pkv_copy_blocks) before
+ *    writing into it.  Full shared blocks are never written, so never copied.
+ * Host memory only; no device access.  Calls on one manager are serialised
+ * by a mutex inside it.  Sequence ids are caller-chosen int64 keys.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* New manager over blocks 0 .. num_blocks-1, all free.  *out = NULL on error. */
+int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Free blocks now (-1 for a NULL manager). */
+int pkv_bm_num_free(const pkv_block_manager* bm);
+
+/* Reference count of a block (0 = free; -1 = bad block id or manager). */
+int pkv_bm_ref_count(const pkv_block_manager* bm, int block);
+
+/* New sequence `seq` of num_tokens tokens (its KV rows are written by the
+ * caller): takes ceil(num_tokens / block_size) blocks.  EINVAL if seq
+ * exists or num_tokens < 0; ENOMEM if too few blocks are free. */
+int pkv_bm_allocate(pkv_block_manager* bm, int64_t seq, int num_tokens);
+
+/* New sequence `child` sharing every block and the length of `parent`
+ * (each shared block's count + 1).  EINVAL if parent is unknown or child
+ * exists. */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Grows `seq` by num_tokens tokens, to be written at positions L ..
+ * L+num_tokens-1.  If L is not a multiple of block_size, num_tokens > 0 and
+ * the last block is shared, that block is copied on write: a fresh block
+ * replaces it in this sequence, and (old, new) is written to
+ * cow_src[0] / cow_dst[0] with *n_cow = 1 (else *n_cow = 0).  Then any
+ * further blocks are taken.  On ENOMEM or EINVAL nothing changes.
+ * cow_src / cow_dst: host arrays of at least one entry. */
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int num_tokens, int32_t* cow_src,
+                  int32_t* cow_dst, int* n_cow);
+
+/* Ends `seq`: each of its blocks loses one reference, and blocks reaching 0
+ * are pushed on the free list in logical order.  EINVAL if unknown. */
+int pkv_bm_release(pkv_block_manager* bm, int64_t seq);
+
+/* Tokens of `seq` (-1 if unknown). */
+int64_t pkv_bm_seq_len(const pkv_block_manager* bm, int64_t seq);
+
+/* Exports rows of the block table for seqs[0..n): table [n,
+ * max_blocks_per_seq] int32 (host), row i = the physical blocks of seqs[i]
+ * in logical order, -1 padded; seqlens [n] int32 (host).  EINVAL if a
+ * sequence is unknown or has more blocks than max_blocks_per_seq. */
+int pkv_bm_table(const pkv_block_manager* bm, const int64_t* seqs, int n,
+                 int max_blocks_per_seq, int32_t* table, int32_t* seqlens);
+
+/*
+ * Copies whole blocks of both pools on the GPU: for i < n, block src[i] of
+ * k_cache and of v_cache ([num_blocks, block_size, num_kv_heads, head_dim])
+ * is copied bit for bit onto block dst[i] (the copy-on-write step above).
+ * src, dst: device int32 arrays; every dst must differ from every src and
+ * from the other dsts.  An id outside [0, num_blocks) sets PKV_ERR_BLOCK and
+ * its pair is skipped.
+ */
+int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
+                    const int32_t* dst, int n, int num_blocks, int block_size, int num_kv_heads,
+                    int head_dim, int32_t* err_flag, void* stream);
 
 #ifdef __cplusplus
 }

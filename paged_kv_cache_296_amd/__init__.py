@@ -21,9 +21,10 @@ __all__ = [
     "varlen_paged", "decode_workspace_bytes", "decode_partition_tokens", "check_decode_args",
     "check_varlen_args", "check_cache_write_args", "check_varlen_paged_args", "status_string",
     "abi_version", "lib_path", "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
+    "BlockManager", "OutOfBlocks", "copy_blocks",
 ]
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENOMEM = 0, 1, 2, 3, 4, 5
 FP32, BF16 = 0, 1
 ERR_BLOCK, ERR_SPAN, ERR_CU, ERR_MAXLEN = 1, 2, 4, 8
 
@@ -74,6 +75,29 @@ def _load():
         L.pkv_varlen_paged.argtypes = [I, P, P, P, P, P, P, I, I, P, I, I, I, I, I, I, I, I, F,
                                        P, P]
         L.pkv_varlen_paged.restype = I
+        I64, PP = ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)
+        L.pkv_bm_create.argtypes = [I, I, PP]
+        L.pkv_bm_create.restype = I
+        L.pkv_bm_destroy.argtypes = [P]
+        L.pkv_bm_destroy.restype = None
+        L.pkv_bm_num_free.argtypes = [P]
+        L.pkv_bm_num_free.restype = I
+        L.pkv_bm_ref_count.argtypes = [P, I]
+        L.pkv_bm_ref_count.restype = I
+        L.pkv_bm_allocate.argtypes = [P, I64, I]
+        L.pkv_bm_allocate.restype = I
+        L.pkv_bm_fork.argtypes = [P, I64, I64]
+        L.pkv_bm_fork.restype = I
+        L.pkv_bm_append.argtypes = [P, I64, I, P, P, P]
+        L.pkv_bm_append.restype = I
+        L.pkv_bm_release.argtypes = [P, I64]
+        L.pkv_bm_release.restype = I
+        L.pkv_bm_seq_len.argtypes = [P, I64]
+        L.pkv_bm_seq_len.restype = I64
+        L.pkv_bm_table.argtypes = [P, P, I, I, P, P]
+        L.pkv_bm_table.restype = I
+        L.pkv_copy_blocks.argtypes = [I, P, P, P, P, I, I, I, I, I, P, P]
+        L.pkv_copy_blocks.restype = I
         _lib = L
     return _lib
 
@@ -366,3 +390,90 @@ def varlen_paged(q, k_cache, v_cache, block_table, cu_seq_lens_q, seqlens_k, max
     if rc:
         raise PkvError(rc, "pkv_varlen_paged")
     return out
+
+
+class OutOfBlocks(PkvError):
+    """Not enough free blocks; the manager is unchanged."""
+
+
+class BlockManager:
+    """Host block manager of one paged pool (free list popped from its end,
+    ref-counted sharing, copy-on-write decisions); native code in libpkv.
+
+    Sequence ids are int keys.  ``append`` returns the copy-on-write pairs
+    (src, dst) the caller must copy on the GPU (``copy_blocks``) before the
+    new tokens are written.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = _load()
+        h = ctypes.c_void_p()
+        rc = self._lib.pkv_bm_create(int(num_blocks), int(block_size), ctypes.byref(h))
+        if rc:
+            raise PkvError(rc, "pkv_bm_create")
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_bm_destroy(h)
+            self._h = None
+
+    def _check(self, rc, what):
+        if rc == ENOMEM:
+            raise OutOfBlocks(rc, what)
+        if rc:
+            raise PkvError(rc, what)
+
+    @property
+    def num_free(self) -> int:
+        return self._lib.pkv_bm_num_free(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return self._lib.pkv_bm_ref_count(self._h, int(block))
+
+    def allocate(self, seq: int, num_tokens: int) -> None:
+        self._check(self._lib.pkv_bm_allocate(self._h, int(seq), int(num_tokens)), "allocate")
+
+    def fork(self, parent: int, child: int) -> None:
+        self._check(self._lib.pkv_bm_fork(self._h, int(parent), int(child)), "fork")
+
+    def append(self, seq: int, num_tokens: int):
+        """Grows seq; returns the list of copy-on-write (src, dst) pairs."""
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int()
+        self._check(self._lib.pkv_bm_append(self._h, int(seq), int(num_tokens), ctypes.byref(src),
+                                            ctypes.byref(dst), ctypes.byref(n)), "append")
+        return [(src.value, dst.value)] if n.value else []
+
+    def release(self, seq: int) -> None:
+        self._check(self._lib.pkv_bm_release(self._h, int(seq)), "release")
+
+    def seq_len(self, seq: int) -> int:
+        return self._lib.pkv_bm_seq_len(self._h, int(seq))
+
+    def table(self, seqs, max_blocks_per_seq: int):
+        """(block_table [n, max_blocks_per_seq], seqlens [n]) as int32 CPU tensors."""
+        ids = (ctypes.c_int64 * len(seqs))(*[int(x) for x in seqs])
+        table = torch.empty((len(seqs), int(max_blocks_per_seq)), dtype=torch.int32)
+        lens = torch.empty(len(seqs), dtype=torch.int32)
+        self._check(self._lib.pkv_bm_table(self._h, ids, len(seqs), int(max_blocks_per_seq),
+                                           ctypes.c_void_p(table.data_ptr()),
+                                           ctypes.c_void_p(lens.data_ptr())), "table")
+        return table, lens
+
+
+def copy_blocks(k_cache, v_cache, src, dst, *, err_flag=None, stream=None):
+    """Copies block src[i] onto block dst[i] in both pools (GPU, in place).
+    src, dst: int32 GPU tensors of equal length."""
+    lib = _load()
+    _need_gpu(k_cache, v_cache, src, dst, err_flag)
+    _need_contig(k_cache=k_cache, v_cache=v_cache, src=src, dst=dst)
+    NB, bs, Hkv, D = _cache_shape(k_cache, v_cache)
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be int32 vectors of one length")
+    rc = lib.pkv_copy_blocks(_dtype_code(k_cache), _ptr(k_cache), _ptr(v_cache), _ptr(src),
+                             _ptr(dst), src.shape[0], NB, bs, Hkv, D, _ptr(err_flag),
+                             _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_copy_blocks")

@@ -133,7 +133,52 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
   }
 }
 
+// Whole-block copies (the copy-on-write step of the block manager): pair
+// blockIdx.y copies block src -> dst of both pools; the workgroups along x
+// split the block into 4 KB pieces per pass of 256 lanes x 16 bytes.
+constexpr int kCopyPieces = 4;  // 16-byte pieces per lane per workgroup
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
+  const int i = blockIdx.y;
+  const int s = a.src[i], d = a.dst[i];
+  if (s < 0 || s >= a.num_blocks || d < 0 || d >= a.num_blocks) {
+    if (a.err_flag && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err_flag, (int)kErrBlock);
+    return;
+  }
+  const long long n16 = a.block_bytes / 16;
+  const long long base = (long long)blockIdx.x * 256 * kCopyPieces + threadIdx.x;
+  const char* ks = (const char*)a.k_cache + (long long)s * a.block_bytes;
+  const char* vs = (const char*)a.v_cache + (long long)s * a.block_bytes;
+  char* kd = (char*)a.k_cache + (long long)d * a.block_bytes;
+  char* vd = (char*)a.v_cache + (long long)d * a.block_bytes;
+  u32x4 kx[kCopyPieces], vx[kCopyPieces];
+#pragma unroll
+  for (int j = 0; j < kCopyPieces; ++j) {
+    const long long c = base + 256 * j;
+    if (c < n16) {
+      kx[j] = *reinterpret_cast<const u32x4*>(ks + 16 * c);
+      vx[j] = *reinterpret_cast<const u32x4*>(vs + 16 * c);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyPieces; ++j) {
+    const long long c = base + 256 * j;
+    if (c < n16) {
+      *reinterpret_cast<u32x4*>(kd + 16 * c) = kx[j];
+      *reinterpret_cast<u32x4*>(vd + 16 * c) = vx[j];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  const long long per_wg = 256LL * 16 * kCopyPieces;
+  const long long gx = (a.block_bytes + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)a.n), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
   if (a.total == 0 && a.batch == 0) return hipSuccess;

@@ -116,6 +116,7 @@ const char* pkv_status_string(int status) {
     case PKV_EUNSUPPORTED: return "unsupported shape or dtype";
     case PKV_EWORKSPACE: return "workspace missing or too small";
     case PKV_EHIP: return "HIP launch failed";
+    case PKV_ENOMEM: return "not enough free blocks";
     default: return "unknown status";
   }
 }
@@ -390,6 +391,32 @@ int pkv_varlen_paged(int dtype, const void* q, const void* k_cache, const void* 
   a.q_tiles = (int)tiles;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipError_t e = pkv::launch_varlen_paged(dtype, head_dim, a, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+
+int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
+                    const int32_t* dst, int n, int num_blocks, int block_size, int num_kv_heads,
+                    int head_dim, int32_t* err_flag, void* stream) {
+  if (n < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PKV_EINVAL;
+  if (dtype != PKV_FP32 && dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (n == 0) return PKV_OK;
+  if (n > 65535) return PKV_EUNSUPPORTED;
+  if (!k_cache || !v_cache || !src || !dst) return PKV_EINVAL;
+  const long long block_bytes =
+      (long long)block_size * num_kv_heads * head_dim * (dtype == PKV_BF16 ? 2 : 4);
+  if (block_bytes % 16 != 0) return PKV_EUNSUPPORTED;
+  pkv::CopyBlocksArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.src = src;
+  a.dst = dst;
+  a.err_flag = err_flag;
+  a.n = n;
+  a.num_blocks = num_blocks;
+  a.block_bytes = block_bytes;
+  hipError_t e = pkv::launch_copy_blocks(a, (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

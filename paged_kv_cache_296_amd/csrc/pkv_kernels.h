@@ -76,6 +76,18 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeAr
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
 hipError_t launch_varlen_paged(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t* err_flag;
+  int n;              // pairs
+  int num_blocks;
+  long long block_bytes;  // block_size * num_kv_heads * head_dim * element size
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 // Table entries one paged-varlen workgroup stages in LDS (bounds max_length_k).
 constexpr int kVarlenMaxTableEntries = 2048;
 // Workgroup shape of the varlen kernel for a q-heads-per-kv-head ratio.
