@@ -20,6 +20,8 @@ The same JSON line carries
                 same workload (about --cpu-seconds of work);
   prefill       the 16-sequence varlen prefill batch: algorithmic TFLOP/s
                 against the 2.5 PFLOP/s dense bf16 MFMA peak;
+  paged_prefill the same batch as a paged step: cache write of the new rows,
+                then varlen attention through the block table;
   mixed_step    the continuous-batching step: 512 decode sequences with the
                 in-place append, then 8 x 1024 prefill tokens, on one stream.
 Only one GPU is supported: --gpus above 1 exits with a message.
