@@ -471,7 +471,13 @@ void varlen_kernel(VarlenArgs a) {
     const float neg_m = softmax_head<D, false>(sc, acc, m_ref, l_run, c, kKeys, hh);
     float psum = 0.f;
     u32 pw[2][8];
+    // the interleaved phase runs at raised wave priority, so that the other
+    // wave on this SIMD fills in around it rather than competing for issue
+    // (measured: 3 % faster; raising it around the P.V MFMAs instead gains
+    // nothing)
+    __builtin_amdgcn_s_setprio(1);
     qk_and_exp<D>((const char*)kbuf(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
+    __builtin_amdgcn_s_setprio(0);
     l_run += psum;
     pv<D>(vbuf(j), voff, pw, acc);
   };
