@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "pkv_kernels.h"
 
 namespace pkv {
@@ -532,12 +534,15 @@ void varlen_kernel(VarlenArgs a) {
 template <int D, bool PAGED>
 hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
   const size_t lds = 4 * Geo<D>::TILEB + (PAGED ? kVarlenMaxTableEntries * sizeof(int) : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
+  // more than 64 KB of dynamic LDS must be allowed once per device
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)varlen_kernel<D, PAGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL((varlen_kernel<D, PAGED>),
                      dim3(a.q_tiles, a.num_heads / a.heads_per_wg, a.batch), dim3(256), lds,
