@@ -714,81 +714,97 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int blo
   }
 }
 
-// Merge of the partials of one (sequence, kv head, chunk of <= 16 q heads),
-// one per run of partitions, one wave: each lane holds the same (q head, D/4
-// dims) it held in the per-partition kernel, so the partials are read back as
-// the contiguous runs they were written as.  m = max m_k,
-// l = sum l_k 2^(m_k - m), sums likewise (in run order), out = sum / l (0 for
-// l = 0); a NaN partial (a data error) makes the output NaN.
+// Merge of the run partials: one thread per 16-byte piece of a partial (4
+// dims of one q head), so a wave reads whole contiguous stretches of the
+// [j][q4][head][4] partial layout and every lane is busy whatever the group
+// size.  Thread t of a (sequence, kv head, chunk of <= 16 heads) holds head
+// t % gc, dims 4E (t / gc % 4) + 4 (t / 4gc) .. +3.  For each head:
+// m = max m_k, l = sum l_k 2^(m_k - m), sums likewise, out = sum / l (0 for
+// l = 0), taken online over batches of 8 runs (a batch's loads all in
+// flight together; the running sums are rescaled when a batch raises m); a
+// NaN partial (a data error) makes the output NaN; empty runs (m = -inf)
+// contribute nothing.
+constexpr int kMergeBatch = 8;
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   using S = Shape<BF16, D>;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const long long gid = (long long)blockIdx.x * 4 + wave;
+  const int per = min(a.group, 16) * (D / 4);  // threads per (sequence, kv head, chunk)
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long grp = gid / per;
+  const int t = (int)(gid - grp * per);
   const long long ngroups = (long long)a.batch * a.num_kv_heads * a.head_chunks;
-  if (gid >= ngroups) return;
-  const int hc = (int)(gid % a.head_chunks);
-  const long long sk = gid / a.head_chunks;  // seq * num_kv_heads + kvh
+  if (grp >= ngroups) return;
+  const int hc = (int)(grp % a.head_chunks);
+  const long long sk = grp / a.head_chunks;  // seq * num_kv_heads + kvh
   const int kvh = (int)(sk % a.num_kv_heads);
   const int seq = (int)(sk / a.num_kv_heads);
-  const int r16 = lane & 15, q4 = lane >> 4;
   const int gc = min(16, a.group - 16 * hc);
-  if (r16 >= gc) return;
-  const int hq = kvh * a.group + 16 * hc + r16;
-  char* dst = (char*)a.out + (((long long)seq * a.num_heads + hq) * D + 4 * S::E * q4) * S::ESZ;
-  float o[4 * S::E];
+  if (t >= gc * (D / 4)) return;
+  const int r = t % gc, q4 = (t / gc) & 3, j = t / (4 * gc);
+  const int hq = kvh * a.group + 16 * hc + r;
+  char* dst = (char*)a.out + (((long long)seq * a.num_heads + hq) * D + 4 * S::E * q4 + 4 * j) *
+                                 S::ESZ;
+  auto store4 = [&](f32x4 o) {
+    if constexpr (BF16)
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    else
+      *reinterpret_cast<f32x4*>(dst) = o;
+  };
 
-  const int L = __builtin_amdgcn_readfirstlane(a.cache_seqlens[seq]);
+  const int L = a.cache_seqlens[seq];
   const int Lp = L + a.has_new;
   if (L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS) {
-#pragma unroll
-    for (int j = 0; j < 4 * S::E; ++j) o[j] = __builtin_nanf("");
-    store_out<BF16, S>(dst, o);
+    const float nan = __builtin_nanf("");
+    store4(f32x4{nan, nan, nan, nan});
     return;
   }
   const int np = Lp > 0 ? (Lp + a.part_tokens - 1) / a.part_tokens : 1;
   // each run of R partitions left one partial, at its first slot
   const int R = a.direct ? 1 : a.ctrl[2];
+  const int nruns = (np + R - 1) / R;
   const long long blk0 = sk * a.n_parts;
-  const float* accp = a.ws_acc + blk0 * a.group * D + 16 * hc * D + 4 * (q4 * gc + r16);
-  const float2* mlp = a.ws_ml + blk0 * a.group + 16 * hc + r16;
-  const long long acc_stride = (long long)a.group * D;  // floats between partitions
+  const float* accp = a.ws_acc + blk0 * a.group * D + 16 * hc * D + 4 * t;
+  const float2* mlp = a.ws_ml + blk0 * a.group + 16 * hc + r;
+  const long long acc_step = (long long)R * a.group * D;  // floats between runs
+  const long long ml_step = (long long)R * a.group;
 
-  // pass 1: the running max over the partials (independent loads)
-  float M = -INFINITY;
+  float M = -INFINITY, Ls = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   bool nan = false;
-#pragma unroll 4
-  for (int k = 0; k < np; k += R) {
-    const float m = mlp[(long long)k * a.group].x;
-    nan |= m != m;
-    M = fmaxf(M, m);
-  }
-  // pass 2: l = sum l_k 2^(m_k - M), sums likewise, in partition order
-  float Ls = 0.f;
+  for (int k0 = 0; k0 < nruns; k0 += kMergeBatch) {
+    float2 ml[kMergeBatch];
+    f32x4 v[kMergeBatch];
 #pragma unroll
-  for (int j = 0; j < 4 * S::E; ++j) o[j] = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 2
-    for (int k = 0; k < np; k += R) {
-      const float2 ml = mlp[(long long)k * a.group];
-      f32x4 v[S::E];
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const bool in = k0 + i < nruns;
+      ml[i] = in ? mlp[(k0 + i) * ml_step] : make_float2(-INFINITY, 0.f);
+      v[i] = in ? *reinterpret_cast<const f32x4*>(accp + (k0 + i) * acc_step)
+                : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mb = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < S::E; ++j)
-        v[j] = *reinterpret_cast<const f32x4*>(accp + k * acc_stride + 16 * j * gc);
-      if (ml.x == -INFINITY) continue;  // an empty partial contributes nothing
-      const float w = fast_exp2(ml.x - M);
-      Ls += ml.y * w;
+    for (int i = 0; i < kMergeBatch; ++i) {
+      nan |= ml[i].x != ml[i].x;
+      mb = fmaxf(mb, ml[i].x);
+    }
+    const float mn = fmaxf(M, mb);
+    if (mn == -INFINITY) continue;  // nothing but empty runs so far
+    if (mn > M) {
+      const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+      Ls *= sc;
+      o *= sc;
+      M = mn;
+    }
 #pragma unroll
-      for (int j = 0; j < S::E; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[4 * j + e] += v[j][e] * w;
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (ml[i].x == -INFINITY) continue;
+      const float w = fast_exp2(ml[i].x - M);
+      Ls += ml[i].y * w;
+      o += v[i] * w;
     }
   }
   const float inv = nan ? __builtin_nanf("") : (Ls > 0.f ? 1.f / Ls : 0.f);
-#pragma unroll
-  for (int j = 0; j < 4 * S::E; ++j) o[j] *= inv;
-  store_out<BF16, S>(dst, o);
+  store4(o * inv);
 }
 
 // Workgroups of the persistent kernel that fit on the device at once; queried
@@ -839,8 +855,9 @@ hipError_t launch_one(const DecodeArgs& args, int phases, hipStream_t stream) {
     }
   }
   if ((phases & 2) && a.n_parts > 1) {
-    const long long groups = (long long)a.batch * a.num_kv_heads * a.head_chunks;
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, BS>), dim3((unsigned)((groups + 3) / 4)),
+    const long long threads = (long long)a.batch * a.num_kv_heads * a.head_chunks *
+                              (a.group < 16 ? a.group : 16) * (D / 4);
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, BS>), dim3((unsigned)((threads + 255) / 256)),
                        dim3(256), 0, stream, a);
     return hipGetLastError();
   }
