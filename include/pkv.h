@@ -99,7 +99,9 @@ int pkv_check_decode_args(int dtype, int has_new, int batch, int num_heads, int 
 /*
  * The split-context partition pkv_decode will use for these arguments, in
  * tokens: either the caller's non-zero partition_tokens, or the library's
- * choice for 0.  A result >= max_blocks_per_seq * block_size means a single
+ * choice for 0 (512 tokens, fewer -- down to 128 -- when the batch is too
+ * small to give every SIMD a unit, the whole row when it is shorter; always
+ * a block multiple).  A result >= max_blocks_per_seq * block_size means a single
  * pass (no partial results and no merge).  Returns -1 when
  * pkv_check_decode_args fails.
  */
