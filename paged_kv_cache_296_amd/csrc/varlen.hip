@@ -52,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kWaveRows = 32;    // query rows per wave
@@ -166,10 +167,20 @@ __device__ __forceinline__ void issue_tile_paged(const char* cache, const int* s
   }
 }
 
-// Reads the K operand of step i of S^T = K Q^T: k-step i / 2, key block i % 2.
+// LDS byte address -> typed LDS pointer.  The operand offsets hold absolute
+// LDS addresses (the dynamic LDS base added once, up front), and the tile
+// offsets are compile-time constants, so every operand read is one register
+// plus an immediate offset.
+template <class T>
+__device__ __forceinline__ T* lds_at(u32 addr) {
+  return (T*)(size_t)addr;
+}
+
+// Reads the K operand of step i of S^T = K Q^T: k-step i / 2, key block i % 2
+// (kt: the tile's byte offset in LDS; koff: the lane's absolute addresses).
 template <int D>
-__device__ __forceinline__ u32x4 k_operand(const char* kt, const int* koff, int i) {
-  return *reinterpret_cast<const u32x4*>(kt + koff[i >> 1] + 32 * (i & 1) * Geo<D>::ROWB);
+__device__ __forceinline__ u32x4 k_operand(u32 kt, const u32* koff, int i) {
+  return *lds_at<lds_u32x4>(kt + koff[i >> 1] + 32 * (i & 1) * Geo<D>::ROWB);
 }
 
 // Masks keys past `valid` (MASK), takes the row max of the tile's scores and
@@ -207,13 +218,18 @@ __device__ __forceinline__ float softmax_head(f32x16 (&s)[2], f32x16* acc, float
 }
 
 // Exponentials of elements 2e, 2e+1 of the flattened scores, packed to bf16.
+// The row sum takes the packed pair (one v_dot2 against (1, 1) instead of two
+// adds), so the normaliser sums exactly the bf16 probabilities that P.V
+// multiplies.
 __device__ __forceinline__ void exp_pair(const f32x16 (&s)[2], int e, float c, float neg_m,
                                          float& psum, u32 (&pw)[2][8]) {
   const int mt = e >> 3, r = 2 * (e & 7);
   const float p0 = fast_exp2(fmaf(s[mt][r], c, neg_m));
   const float p1 = fast_exp2(fmaf(s[mt][r + 1], c, neg_m));
-  psum += p0 + p1;
-  pw[mt][r >> 1] = pack_bf16x2(p0, p1);
+  const u32 w = pack_bf16x2(p0, p1);
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, psum, false);
+  pw[mt][r >> 1] = w;
 }
 
 // S^T of the next tile (16 MFMAs, K operand read four steps ahead) with the
@@ -221,7 +237,7 @@ __device__ __forceinline__ void exp_pair(const f32x16 (&s)[2], int e, float c, f
 // core and the vector ALU of one wave work at the same time.  The scheduling
 // fences keep this interleaving and keep the K reads from all being hoisted.
 template <int D>
-__device__ __forceinline__ void qk_and_exp(const char* kt, const u32x4* qr, const int* koff,
+__device__ __forceinline__ void qk_and_exp(u32 kt, const u32x4* qr, const u32* koff,
                                            f32x16 (&sn)[2], const f32x16 (&sc)[2], float c,
                                            float neg_m, float& psum, u32 (&pw)[2][8]) {
   using G = Geo<D>;
@@ -248,7 +264,7 @@ __device__ __forceinline__ void qk_and_exp(const char* kt, const u32x4* qr, cons
 
 // S^T of one tile alone (the first tile).
 template <int D>
-__device__ __forceinline__ void qk_only(const char* kt, const u32x4* qr, const int* koff,
+__device__ __forceinline__ void qk_only(u32 kt, const u32x4* qr, const u32* koff,
                                         f32x16 (&sn)[2]) {
   using G = Geo<D>;
   constexpr int NQK = 2 * G::KS;
@@ -274,16 +290,16 @@ __device__ __forceinline__ void qk_only(const char* kt, const u32x4* qr, const i
 // the two transposing reads fetch V^T for exactly those keys.  The reads run
 // two MFMAs ahead.
 template <int D>
-__device__ __forceinline__ void pv(lds_char* vt, const int* voff, const u32 (&pw)[2][8],
+__device__ __forceinline__ void pv(u32 vt, const u32* voff, const u32 (&pw)[2][8],
                                    f32x16* acc) {
   using G = Geo<D>;
   constexpr int NPV = 4 * G::DT;
   auto vread = [&](int i) {
     const int kc = i / G::DT, d = i % G::DT;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(vt + voff[2 * d] + 16 * kc * G::ROWB));
+        lds_at<lds_i16x4>(vt + voff[2 * d] + 16 * kc * G::ROWB));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(vt + voff[2 * d + 1] + 16 * kc * G::ROWB));
+        lds_at<lds_i16x4>(vt + voff[2 * d + 1] + 16 * kc * G::ROWB));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   i16x8 vf[2];
@@ -411,10 +427,14 @@ void varlen_kernel(VarlenArgs a) {
     const int r = cl / G::CH, ps = cl % G::CH;
     loff[i] = (PAGED ? 0 : r * tok_k) + 16 * (ps ^ swz<D>(r));
   }
-  int koff[G::KS];
+  const u32 lbase = (u32)(uintptr_t)lds;
+  u32 koff[G::KS];
 #pragma unroll
-  for (int ks = 0; ks < G::KS; ++ks) koff[ks] = n * G::ROWB + 16 * ((2 * ks + hh) ^ swz<D>(n));
-  int voff[2 * G::DT];
+  for (int ks = 0; ks < G::KS; ++ks) {
+    koff[ks] = lbase + n * G::ROWB + 16 * ((2 * ks + hh) ^ swz<D>(n));
+    asm volatile("" : "+v"(koff[ks]));  // keep the sum: not re-split into base + offset per read
+  }
+  u32 voff[2 * G::DT];
   {
     const int q16 = lane & 15, grp = (lane >> 4) & 1;
 #pragma unroll
@@ -423,7 +443,7 @@ void varlen_kernel(VarlenArgs a) {
       for (int r = 0; r < 2; ++r) {
         const int vr = 8 * r + 4 * hh + (q16 >> 2);
         const int lc = 4 * d + 2 * grp + ((q16 >> 1) & 1);
-        voff[2 * d + r] = vr * G::ROWB + 16 * (lc ^ swz<D>(vr)) + 8 * (q16 & 1);
+        voff[2 * d + r] = lbase + vr * G::ROWB + 16 * (lc ^ swz<D>(vr)) + 8 * (q16 & 1);
       }
   }
 
@@ -443,6 +463,8 @@ void varlen_kernel(VarlenArgs a) {
   const bool partial = last_valid < kKeys;
   auto kbuf = [&](int j) { return lds + (j & 1) * G::TILEB; };
   auto vbuf = [&](int j) { return lds + (2 + (j & 1)) * G::TILEB; };
+  auto kofs = [&](int j) { return (u32)((j & 1) * G::TILEB); };        // byte offsets of the
+  auto vofs = [&](int j) { return (u32)((2 + (j & 1)) * G::TILEB); };  // same tiles
   auto issue = [&](const char* g, int j, lds_char* tile) {
     if constexpr (PAGED) {
       if (j + 1 < nk || !partial)
@@ -478,17 +500,17 @@ void varlen_kernel(VarlenArgs a) {
     // (measured: 3 % faster; raising it around the P.V MFMAs instead gains
     // nothing)
     __builtin_amdgcn_s_setprio(1);
-    qk_and_exp<D>((const char*)kbuf(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
+    qk_and_exp<D>(kofs(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
     __builtin_amdgcn_s_setprio(0);
     l_run += psum;
-    pv<D>(vbuf(j), voff, pw, acc);
+    pv<D>(vofs(j), voff, pw, acc);
   };
   if (nk > 0) {
     issue(kg, 0, kbuf(0));
     issue(vg, 0, vbuf(0));
     if (nk > 1) issue(kg, 1, kbuf(1));
     wait_all();
-    if (wave_active) qk_only<D>((const char*)kbuf(0), qr, koff, sa);
+    if (wave_active) qk_only<D>(kofs(0), qr, koff, sa);
     int j = 0;
     for (; j + 2 < nk; j += 2) {
       step(j, sa, sb);
@@ -511,7 +533,7 @@ void varlen_kernel(VarlenArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) exp_pair(sa, e, c, neg_m, psum, pw);
       l_run += psum;
-      pv<D>(vbuf(j), voff, pw, acc);
+      pv<D>(vofs(j), voff, pw, acc);
     }
   }
 
