@@ -140,3 +140,21 @@ def test_product_path_refuses_cpu_tensors(pkv):
         pkv.cache_write(torch.zeros(1, 4, 4, 64), torch.zeros(1, 4, 4, 64), cu, sl, kc, kc.clone(), bt)
     with pytest.raises(ValueError, match="GPU"):
         pkv.varlen_paged(torch.zeros(1, 4, 4, 64), kc, kc.clone(), bt, cu, sl, 4, 4)
+
+
+def test_library_partition_rule(pkv):
+    # 512 tokens for batches that give every SIMD a unit (the GQA-4 and
+    # long-context shapes), whatever the row span beyond it
+    assert pkv.decode_partition_tokens(64, 32, 8, 128, 16, 256, 0) == 512
+    assert pkv.decode_partition_tokens(256, 64, 8, 128, 16, 2048, 0) == 512
+    assert pkv.decode_partition_tokens(512, 32, 8, 128, 16, 513, 0) == 512
+    # a row shorter than the partition: one pass over the whole row
+    assert pkv.decode_partition_tokens(256, 32, 8, 128, 16, 20, 0) == 320
+    # ... unless too few units: 64 x 8 one-pass units are split into 128-token parts
+    assert pkv.decode_partition_tokens(64, 32, 8, 128, 16, 20, 0) == 128
+    # too few units at 512: halved, but never below 128 tokens
+    assert pkv.decode_partition_tokens(1, 8, 8, 128, 16, 8192, 0) == 512
+    assert pkv.decode_partition_tokens(1, 8, 2, 128, 16, 512, 0) == 128
+    assert pkv.decode_partition_tokens(1, 8, 1, 128, 32, 4096, 0) == 128
+    # an explicit partition is kept as given
+    assert pkv.decode_partition_tokens(64, 32, 8, 128, 16, 256, 1024) == 1024
