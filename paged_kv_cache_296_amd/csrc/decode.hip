@@ -626,14 +626,19 @@ void decode_direct_kernel(DecodeArgs a) {
 // Work list for the persistent kernel, one workgroup.  Every sequence's
 // partitions are cut into runs of R consecutive partitions (R chosen so that
 // there are at least about four units per resident wave, and at most
-// a.max_run); full runs of all sequences come first, then each sequence's
-// shorter last run.  A sequence with nothing to attend or a bad length gets
-// one one-partition run so that its output is written.  Items carry
-// (sequence, first partition << 8 | partitions, cached length).  Also resets
-// the ticket counter and records the run length for the merge.
+// a.max_run).  The runs that do not hold a sequence's end are all R full
+// partitions long and come first, in sequence order; then each sequence's
+// last run, longest first (bucketed by token count), so that the list ends
+// on the shortest units and the waves run dry together.  A sequence with
+// nothing to attend or a bad length gets one one-partition run so that its
+// output is written.  Items carry (sequence, first partition << 8 |
+// partitions, cached length).  Also resets the ticket counter and records
+// the run length for the merge.
+constexpr int kPlanBuckets = 512;
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int block_size) {
-  __shared__ int s_a[1024], s_b[1024];
-  __shared__ int carry_a, carry_b, total_a, run;
+  __shared__ int s_a[1024];
+  __shared__ int s_hist[kPlanBuckets], s_cur[kPlanBuckets];
+  __shared__ int carry, run;
   const int tid = threadIdx.x;
   const long long span = (long long)a.max_blocks_per_seq * block_size;
   auto nparts_of = [&](int i, int& L) {
@@ -663,53 +668,69 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int blo
   if (tid == 0) {
     long long r = units / (4LL * a.resident_waves);
     run = (int)(r < 1 ? 1 : (r > a.max_run ? a.max_run : r));
-  }
-  __syncthreads();
-  const int R = run;
-  // pass 2: number of full runs over the batch
-  my = 0;
-  for (int i = tid; i < a.batch; i += 1024) {
-    int L;
-    my += nparts_of(i, L) / R;
-  }
-  const int full_total = block_sum(my);
-  if (tid == 0) {
-    total_a = full_total;
-    carry_a = 0;
-    carry_b = 0;
+    carry = 0;
     a.ctrl[0] = 0;
   }
+  for (int b = tid; b < kPlanBuckets; b += 1024) s_hist[b] = s_cur[b] = 0;
   __syncthreads();
-  // pass 3: exclusive scans in chunks of 1024 sequences, then write items
+  const int R = run;
+  const long long rp = (long long)R * a.part_tokens;  // tokens of a full run
+  // a sequence's last run: its first partition, and the bucket of its token
+  // count (0 = a full run's length, kPlanBuckets-1 = nothing)
+  auto last_run = [&](int np, int L, int& first) {
+    first = ((np - 1) / R) * R;
+    const int Lp = L + a.has_new;
+    const long long t = (L < 0 || (long long)Lp > span) ? 0 : max(Lp - first * a.part_tokens, 0);
+    return (int)((rp - t) * kPlanBuckets / (rp + 1));
+  };
+  // pass 2: runs before each sequence's last, scanned in chunks of 1024
+  // sequences and written in sequence order; the last runs are counted per
+  // bucket
   for (int base = 0; base < a.batch; base += 1024) {
     const int i = base + tid;
-    int L = 0, np = 0;
-    if (i < a.batch) np = nparts_of(i, L);
-    const int nf = np / R, nr = (np % R) ? 1 : 0;
-    s_a[tid] = nf;
-    s_b[tid] = nr;
+    int L = 0, np = 0, first = 0;
+    if (i < a.batch) {
+      np = nparts_of(i, L);
+      atomicAdd(&s_hist[last_run(np, L, first)], 1);
+    }
+    const int nc = np > 0 ? (np - 1) / R : 0;
+    s_a[tid] = nc;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-      const int va = tid >= off ? s_a[tid - off] : 0;
-      const int vb = tid >= off ? s_b[tid - off] : 0;
+      const int v = tid >= off ? s_a[tid - off] : 0;
       __syncthreads();
-      s_a[tid] += va;
-      s_b[tid] += vb;
+      s_a[tid] += v;
       __syncthreads();
     }
-    const int ea = carry_a + s_a[tid] - nf;  // exclusive offsets
-    const int eb = carry_b + s_b[tid] - nr;
-    for (int k = 0; k < nf; ++k) a.items[ea + k] = make_int4(i, ((k * R) << 8) | R, L, 0);
-    if (nr) a.items[total_a + eb] = make_int4(i, ((nf * R) << 8) | (np % R), L, 0);
+    const int e = carry + s_a[tid] - nc;  // exclusive offset
+    for (int k = 0; k < nc; ++k) a.items[e + k] = make_int4(i, ((k * R) << 8) | R, L, 0);
     __syncthreads();
-    if (tid == 1023) {
-      carry_a += s_a[1023];
-      carry_b += s_b[1023];
-    }
+    if (tid == 1023) carry += s_a[1023];
     __syncthreads();
   }
+  const int n_lead = carry;
+  // bucket starts: exclusive scan of the histogram (kPlanBuckets <= 1024)
+  const int h = tid < kPlanBuckets ? s_hist[tid] : 0;
+  s_a[tid] = h;
+  __syncthreads();
+  for (int off = 1; off < kPlanBuckets; off <<= 1) {
+    const int v = tid >= off ? s_a[tid - off] : 0;
+    __syncthreads();
+    s_a[tid] += v;
+    __syncthreads();
+  }
+  if (tid < kPlanBuckets) s_hist[tid] = s_a[tid] - h;
+  __syncthreads();
+  // pass 3: the last runs, longest first (order within a bucket is free)
+  for (int i = tid; i < a.batch; i += 1024) {
+    int L, first;
+    const int np = nparts_of(i, L);
+    const int b = last_run(np, L, first);
+    const int pos = s_hist[b] + atomicAdd(&s_cur[b], 1);
+    a.items[n_lead + pos] = make_int4(i, (first << 8) | (np - first), L, 0);
+  }
   if (tid == 0) {
-    a.ctrl[1] = total_a + carry_b;
+    a.ctrl[1] = n_lead + a.batch;
     a.ctrl[2] = R;
   }
 }
