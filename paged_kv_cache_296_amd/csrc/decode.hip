@@ -625,7 +625,7 @@ void decode_direct_kernel(DecodeArgs a) {
 
 // Work list for the persistent kernel, one workgroup.  Every sequence's
 // partitions are cut into runs of R consecutive partitions (R chosen so that
-// there are at least about four units per resident wave, and at most
+// there are at least about three units per resident wave, and at most
 // a.max_run).  The runs that do not hold a sequence's end are all R full
 // partitions long and come first, in sequence order; then each sequence's
 // last run, longest first (bucketed by token count), so that the list ends
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int blo
   }
   const long long units = (long long)block_sum(my) * a.num_kv_heads * a.head_chunks;
   if (tid == 0) {
-    long long r = units / (4LL * a.resident_waves);
+    long long r = units / (3LL * a.resident_waves);
     run = (int)(r < 1 ? 1 : (r > a.max_run ? a.max_run : r));
     carry = 0;
     a.ctrl[0] = 0;
