@@ -853,8 +853,9 @@ hipError_t launch_one(const DecodeArgs& args, int phases, hipStream_t stream) {
   const auto kernel = decode_partial_kernel<BF16, D, BS>;
   long long wgs = resident_workgroups(kernel, kWaves * 64);
   a.resident_waves = (int)(wgs * kWaves);
-  // few units: the direct grid; many: the persistent kernel with runs
-  a.direct = a.total_units <= 4LL * a.resident_waves;
+  // few units (up to two grid slots per resident wave): the direct grid;
+  // more: the persistent kernel with runs
+  a.direct = a.total_units <= 2LL * a.resident_waves;
   if ((phases & 1) && a.direct) {
     const long long grid = (a.total_units + kWaves - 1) / kWaves;
     if (grid > 0) {
