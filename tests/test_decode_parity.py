@@ -302,3 +302,17 @@ def test_runs_of_partitions(pt):
                                  lengths=lengths.tolist(), num_blocks=8000, append=True,
                                  partition_tokens=pt, device=DEV)
     run_case(case, "bf16")
+
+
+@pytest.mark.parametrize("pt", [16, 48])
+def test_large_batch_work_list(pt):
+    """More than 1024 sequences through the persistent kernel: the work list
+    is planned in chunks of 1024 sequences, runs of several partitions lead,
+    and every sequence's last run is placed longest first across the whole
+    batch.  Lengths include 0 (nothing cached, the new token only)."""
+    lengths = np.random.default_rng(4100 + pt).integers(0, 300, size=1500)
+    lengths[:4] = [0, 1, pt, 299]
+    case = workloads.make_decode(seed=4100 + pt, dtype="bf16", batch=1500, num_heads=8,
+                                 num_kv_heads=2, head_dim=128, block_size=16, lengths=lengths,
+                                 num_blocks=20000, append=True, partition_tokens=pt, device=DEV)
+    run_case(case, "bf16")
