@@ -497,8 +497,9 @@ void varlen_kernel(VarlenArgs a) {
     u32 pw[2][8];
     // the interleaved phase runs at raised wave priority, so that the other
     // wave on this SIMD fills in around it rather than competing for issue
-    // (measured: 3 % faster; raising it around the P.V MFMAs instead gains
-    // nothing)
+    // (3 % faster when the loop still summed with fp32 adds; with the
+    // current loop, priority 0, 1 or 3, or raising it from the max on, all
+    // measure within run-to-run noise)
     __builtin_amdgcn_s_setprio(1);
     qk_and_exp<D>(kofs(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
     __builtin_amdgcn_s_setprio(0);
