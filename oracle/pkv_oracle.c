@@ -419,7 +419,7 @@ int pkvo_cache_write(int dtype, const void* k, const void* v, const int32_t* cu,
   const size_t row_bytes = (size_t)Hkv * D * elem_size(dtype);
   for (int b = 0; b < batch; ++b)
     for (int i = 0; i < cu[b + 1] - cu[b]; ++i) {
-      int32_t w[3];
+      int32_t w[3] = {0, 0, 0};  /* every slot was located above */
       pkvo_locate(block_table, max_blocks_per_seq, num_blocks, bs, b, start[b] + i, w);
       const int64_t slot = (int64_t)w[2] * bs + w[1];
       const int64_t r = cu[b] + i;

@@ -115,7 +115,9 @@ __device__ __forceinline__ u32x4 vsharp(const char* base, int bytes) {
 // flight: it would otherwise wait for every such load before each
 // transposing LDS read.  The loop waits for these loads itself (vmcnt(0) and
 // a barrier before a stage is read).  One wait state is needed between the
-// M0 write and the load.
+// M0 write and the load.  The compiler treats m0 as reserved and warns that
+// it may not honour the clobber; nothing else in these kernels uses m0 (the
+// generated code has no other m0 access), so the value left there is dead.
 __device__ __forceinline__ void load_to_lds(u32x4 rs, int voff, u32 lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
