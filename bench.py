@@ -53,6 +53,11 @@ def kv_bytes(case):
     return int(case.attended.sum()) * 2 * Hkv * D * elt
 
 
+# the per-partition kernel each decode workload runs: the persistent kernel,
+# or the direct grid for few units (up to two grid slots per resident wave)
+DECODE_KERNEL = {"decode_b64_gqa4": "decode_direct_kernel", "tiny_decode_fp32": "decode_direct_kernel"}
+
+
 def varlen_flops(case):
     """Algorithmic flops: sum_b 4 * D * Hq * len_q * len_k (QK^T and P.V)."""
     _, _, Hq, D = case.q.shape
@@ -329,7 +334,8 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "queries_per_s": round(B / (wall * 1e-3), 1),
         "kernels_ms": {"decode_partial": round(part_ms, 4), "decode_merge": round(merge_ms, 4)},
-        "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel", "achieved": round(ach, 2),
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL.get(args.workload, "decode_partial_kernel"),
+                     "achieved": round(ach, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("decode.hip", args.workload)},
     }
