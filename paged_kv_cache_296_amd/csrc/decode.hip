@@ -105,6 +105,16 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
          ((u32)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
+// Cache policy of the K/V tile loads (the buffer instructions' aux bits:
+// 1 = sc0, 2 = nt, 16 = sc1).  The persistent kernel streams each K/V byte
+// once per call through a working set far above the 256 MB last-level
+// cache, and the non-temporal hint measured 4 % faster there (long-context
+// batch 5.93 -> 6.16 TB/s, the mixed step's decode half 5.96 -> 6.39).  The
+// direct grid serves small batches whose K/V partly stays cached from one
+// decode step to the next; the hint costs it 6 % (64 sequences, 4.91 -> 4.58
+// TB/s), sc1 13 %, so it keeps the default policy.
+constexpr int kCpolStream = 2;
+constexpr int kCpolDefault = 0;
 constexpr int kRsrcFlags = 0x00020000;  // gfx9-family buffer descriptor word 3
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* base, int bytes) {
@@ -112,19 +122,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* base, int byt
 }
 
 // V words of one token for this lane: E elements at byte voff + soff.
-template <bool BF16, class S>
+template <bool BF16, class S, int CPOL>
 __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                        typename Words<BF16>::word* w) {
   using W = Words<BF16>;
   if constexpr (S::VW == 2) {
-    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, CPOL);
     const typename W::vec2 y = __builtin_bit_cast(typename W::vec2, x);
     w[0] = y[0];
     w[1] = y[1];
   } else {
 #pragma unroll
     for (int j = 0; j < S::VW / 4; ++j) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * j, soff, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * j, soff, CPOL);
       const typename W::vec y = __builtin_bit_cast(typename W::vec, x);
       w[4 * j] = y[0];
       w[4 * j + 1] = y[1];
@@ -138,7 +148,7 @@ __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t r, int voff, int s
 // token row of this kv head (uniform, 64-bit scalar); `bytes` is what is left
 // of the physical block from there, so the buffer descriptors bound every
 // access to the block.  koff/voff are the lane's loop-invariant offsets.
-template <bool BF16, class S>
+template <bool BF16, class S, int CPOL>
 __device__ __forceinline__ void load_tile(Tile<BF16, S>& r, const char* tk, const char* tv,
                                           int bytes, int koff, int voff, int tok) {
   using W = Words<BF16>;
@@ -146,9 +156,9 @@ __device__ __forceinline__ void load_tile(Tile<BF16, S>& r, const char* tk, cons
 #pragma unroll
   for (int t = 0; t < S::NKL; ++t)
     r.k[t] = __builtin_bit_cast(typename W::vec,
-                                __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * t, 0, 0));
+                                __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * t, 0, CPOL));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_v<BF16, S>(rv, voff, i * tok, r.v[i]);
+  for (int i = 0; i < 4; ++i) load_v<BF16, S, CPOL>(rv, voff, i * tok, r.v[i]);
 }
 
 // A one-token tile holding the new token (token 0; every other slot zero),
@@ -294,7 +304,7 @@ __device__ __forceinline__ void store_out(char* dst, const float* o) {
 // the slot of its first partition.  (A global store in mid-stream would make
 // every later tile wait also wait for the store's acknowledgement: the
 // vector-memory counter retires loads and stores in order.)
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, int CPOL>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, float* run_w,
                                             int lane, int seq, int p0, int nparts, int L, int kvh,
                                             int hc) {
@@ -486,7 +496,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
     const int pb = __builtin_amdgcn_readfirstlane(slice_w[(16 * t) / BS]);
     const int inblk = (16 * t) % BS;
     const long long off = (long long)pb * blk + (long long)inblk * tok;
-    load_tile<BF16, S>(r, kbase + off, vbase + off, (BS - inblk) * tok, koff, voff, tok);
+    load_tile<BF16, S, CPOL>(r, kbase + off, vbase + off, (BS - inblk) * tok, koff, voff, tok);
   };
   // a partition ends after tile t: write its partial (the run's last
   // partition is written after the loop)
@@ -590,7 +600,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int4 item = a.items[u / (unsigned)per_item];
     const int r = (int)(u % (unsigned)per_item);
     const int packed = __builtin_amdgcn_readfirstlane(item.y);
-    decode_unit<BF16, D, BS>(a, slice[wave], run_state[wave], lane,
+    decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane,
                              __builtin_amdgcn_readfirstlane(item.x),
                              packed >> 8, packed & 255, __builtin_amdgcn_readfirstlane(item.z),
                              r / a.head_chunks, r % a.head_chunks);
@@ -620,7 +630,7 @@ void decode_direct_kernel(DecodeArgs a) {
   const int Lp = L + a.has_new;
   const bool bad = L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS;
   if (part > 0 && (bad || part * a.part_tokens >= Lp)) return;
-  decode_unit<BF16, D, BS>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh, hc);
+  decode_unit<BF16, D, BS, kCpolDefault>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh, hc);
 }
 
 // Work list for the persistent kernel, one workgroup.  Every sequence's
