@@ -15,7 +15,11 @@
 // pieces, issuing the loads of all 4 rows of K and V before any store, so
 // each lane has 16 loads in flight.  A row is contiguous at both ends (a
 // token row of the cache is [Hkv][D] like a packed row), so both sides are
-// coalesced.  HBM bound: 2 reads + 2 writes of the row per packed row.
+// coalesced.  The packed rows are read once, with the non-temporal hint
+// (measured 28 % faster than plain loads on the 16-request prefill batch:
+// 55.5 -> 40.0 us with the last-level cache flushed before each call; the
+// same hint on the stores changed nothing).  HBM bound: 2 reads + 2 writes
+// of the row per packed row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,6 +33,11 @@ constexpr int kWavesPerGroup = 4;
 constexpr int kRowsPerWave = 4;   // rows one wave copies, all loads in flight together
 constexpr int kMaxPieces = 4;     // 16-byte pieces per lane per row (row_bytes <= 4 KB)
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u, kErrCu = 4u;
+
+// 16 bytes read once: non-temporal load (global_load_dwordx4 ... nt)
+__device__ __forceinline__ u32x4 load_once(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // The request of packed row r: the last b with cu[b] <= r.  Up to 63
 // requests: one load of cu per lane and a ballot; more: a binary search on
@@ -107,8 +116,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
     for (int j = 0; j < kMaxPieces; ++j) {
       const int c = lane + 64 * j;
       if (ok[i] && c < n16) {
-        kx[i][j] = *reinterpret_cast<const u32x4*>((const char*)a.k + src[i] + 16 * c);
-        vx[i][j] = *reinterpret_cast<const u32x4*>((const char*)a.v + src[i] + 16 * c);
+        kx[i][j] = load_once((const char*)a.k + src[i] + 16 * c);
+        vx[i][j] = load_once((const char*)a.v + src[i] + 16 * c);
       }
     }
 #pragma unroll
@@ -125,8 +134,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
   for (int i = 0; i < kRowsPerWave; ++i) {
     if (!ok[i]) continue;
     for (int c = lane + 64 * kMaxPieces; c < n16; c += 64) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>((const char*)a.k + src[i] + 16 * c);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>((const char*)a.v + src[i] + 16 * c);
+      const u32x4 kv = load_once((const char*)a.k + src[i] + 16 * c);
+      const u32x4 vv = load_once((const char*)a.v + src[i] + 16 * c);
       *reinterpret_cast<u32x4*>((char*)a.k_cache + dst[i] + 16 * c) = kv;
       *reinterpret_cast<u32x4*>((char*)a.v_cache + dst[i] + 16 * c) = vv;
     }
@@ -135,7 +144,9 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
 
 // Whole-block copies (the copy-on-write step of the block manager): pair
 // blockIdx.y copies block src -> dst of both pools; the workgroups along x
-// split the block into 4 KB pieces per pass of 256 lanes x 16 bytes.
+// split the block into 4 KB pieces per pass of 256 lanes x 16 bytes.  The
+// source blocks are read with the non-temporal hint (4096 pairs of 32 KB
+// bf16 blocks, cache flushed: 3.84-3.94 -> 4.83 TB/s moved).
 constexpr int kCopyPieces = 4;  // 16-byte pieces per lane per workgroup
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   const int i = blockIdx.y;
@@ -155,8 +166,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   for (int j = 0; j < kCopyPieces; ++j) {
     const long long c = base + 256 * j;
     if (c < n16) {
-      kx[j] = *reinterpret_cast<const u32x4*>(ks + 16 * c);
-      vx[j] = *reinterpret_cast<const u32x4*>(vs + 16 * c);
+      kx[j] = load_once(ks + 16 * c);
+      vx[j] = load_once(vs + 16 * c);
     }
   }
 #pragma unroll
