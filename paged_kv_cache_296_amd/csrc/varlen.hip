@@ -320,11 +320,12 @@ __device__ __forceinline__ void pv(u32 vt, const u32* voff, const u32 (&pw)[2][8
   }
 }
 
-// PAGED = false: keys packed like the queries (cu_k); true: keys are the
-// first seqlens_k[b] tokens of sequence b in the paged cache (block_table).
+// One work item: q-row tile qt of request b, q heads hy * heads_per_wg ..
+// (+ heads_per_wg - 1).  PAGED = false: keys packed like the queries (cu_k);
+// true: keys are the first seqlens_k[b] tokens of sequence b in the paged
+// cache (block_table).  Every exit is uniform over the workgroup.
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void varlen_kernel(VarlenArgs a) {
+__device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy, int b) {
   using G = Geo<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -332,8 +333,7 @@ void varlen_kernel(VarlenArgs a) {
   const int n = lane & 31, hh = lane >> 5;
   const int hpw = a.heads_per_wg, rb = kWaves / hpw;
   const int hw = wave % hpw, rbi = wave / hpw;
-  const int qt = blockIdx.x, b = blockIdx.z;
-  const int h0 = blockIdx.y * hpw;
+  const int h0 = hy * hpw;
   const int wg_rows = kWaveRows * rb;
 
   const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
@@ -360,7 +360,7 @@ void varlen_kernel(VarlenArgs a) {
   // A request the kernel cannot run: flag it and write NaN to its rows (when
   // the rows themselves can be located).
   auto fail = [&](unsigned bit) {
-    if (a.err_flag && tid == 0 && qt == 0 && blockIdx.y == 0) atomicOr(a.err_flag, (int)bit);
+    if (a.err_flag && tid == 0 && qt == 0 && hy == 0) atomicOr(a.err_flag, (int)bit);
     if (!(q0 >= 0 && q1 >= q0 && q1 <= a.total_q)) return;  // nowhere safe to write
     const int r0 = qt * wg_rows, r1 = min(len_q, r0 + wg_rows);
     for (int i = tid; i < (r1 > r0 ? (r1 - r0) * hpw : 0); i += 256) {
@@ -556,22 +556,149 @@ void varlen_kernel(VarlenArgs a) {
     }
 }
 
+// One workgroup per item of the full (q tile, head group, request) grid;
+// items past a request's rows exit at once.
 template <int D, bool PAGED>
-hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
-  const size_t lds = 4 * Geo<D>::TILEB + (PAGED ? kVarlenMaxTableEntries * sizeof(int) : 0);
-  // more than 64 KB of dynamic LDS must be allowed once per device
-  static std::atomic<bool> attr_set[64];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void varlen_kernel(VarlenArgs a) {
+  varlen_item<D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Persistent form for batches of up to kPersistMaxBatch requests: as many
+// workgroups as fit on the device, each building the same item list in LDS
+// -- only the q tiles a request has, requests ranked by key-tile count,
+// longest first -- and taking items k * G + w (k even) or k * G + G - 1 - w
+// (k odd) of it, so that every workgroup gets a similar mix of long and
+// short items and the list ends on the shortest ones.  Saves the launch and
+// request lookups of the empty and the per-tile workgroups and drains the
+// tail in order.
+constexpr int kPersistMaxBatch = 256;
+template <int D>
+constexpr int persist_list_offset(bool paged) {
+  return 4 * Geo<D>::TILEB + (paged ? kVarlenMaxTableEntries * (int)sizeof(int) : 0);
+}
+constexpr int kPersistListBytes = (4 * kPersistMaxBatch + 1) * (int)sizeof(int);
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void varlen_persistent_kernel(VarlenArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int* ord = reinterpret_cast<int*>(smem + persist_list_offset<D>(PAGED));  // rank -> request
+  int* pre = ord + kPersistMaxBatch;        // [B + 1] items before rank r
+  int* key = pre + kPersistMaxBatch + 1;    // key tiles, then scan scratch
+  int* nqt = key + kPersistMaxBatch;        // q tiles of request b
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  const int hpw = a.heads_per_wg, hg = a.num_heads / hpw;
+  const int wg_rows = kWaveRows * (kWaves / hpw);
+  if (tid < B) {
+    // the q tiles the full grid would give this request (at least one, so
+    // that its lengths are checked); key tiles for the ranking only
+    long long lq = (long long)a.cu_q[tid + 1] - a.cu_q[tid];
+    lq = lq < 0 ? 0 : (lq > (long long)a.q_tiles * wg_rows ? (long long)a.q_tiles * wg_rows : lq);
+    const int t = (int)((lq + wg_rows - 1) / wg_rows);
+    nqt[tid] = t > 0 ? t : 1;
+    long long lk = PAGED ? (long long)a.seqlens_k[tid] : (long long)a.cu_k[tid + 1] - a.cu_k[tid];
+    lk = lk < 0 ? 0 : (lk > a.max_len_k ? a.max_len_k : lk);
+    key[tid] = (int)((lk + kKeys - 1) / kKeys);
+  }
+  __syncthreads();
+  if (tid < B) {
+    const int kb = key[tid];
+    int r = 0;
+    for (int j = 0; j < B; ++j) {
+      const int kj = key[j];
+      r += (kj > kb) || (kj == kb && j < tid);
+    }
+    ord[r] = tid;
+  }
+  __syncthreads();
+  // inclusive scan of the items in rank order
+  key[tid] = tid < B ? nqt[ord[tid]] * hg : 0;
+  __syncthreads();
+  for (int off = 1; off < kPersistMaxBatch; off <<= 1) {
+    const int v = tid >= off ? key[tid - off] : 0;
+    __syncthreads();
+    key[tid] += v;
+    __syncthreads();
+  }
+  if (tid < B) pre[tid + 1] = key[tid];
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+  const int total = pre[B];
+  const int G = gridDim.x, w = blockIdx.x;
+  for (int k = 0;; ++k) {
+    const long long item = (long long)k * G + ((k & 1) ? G - 1 - w : w);
+    if (item >= total) break;
+    int lo = 0, hi = B;  // pre[lo] <= item < pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= item) lo = mid;
+      else hi = mid;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(ord[lo]);
+    const int rem = (int)item - pre[lo];
+    const int t = nqt[b];
+    const int hy = __builtin_amdgcn_readfirstlane(rem / t);
+    const int qt = __builtin_amdgcn_readfirstlane(rem - (rem / t) * t);
+    __syncthreads();  // every wave is done with the previous item's tiles
+    varlen_item<D, PAGED>(a, qt, hy, b);
+  }
+}
+
+// Dynamic LDS above 64 KB must be allowed once per device and kernel.
+template <class K>
+hipError_t allow_lds(K kernel, size_t lds) {
+  static std::atomic<bool> done[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)varlen_kernel<D, PAGED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
+  if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev].store(true, std::memory_order_release);
+  return e;
+}
+
+// Workgroups of the persistent kernel that fit on the device at once
+// (launch geometry only), per device.
+template <class K>
+int persistent_workgroups(K kernel, size_t lds) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
   }
-  hipLaunchKernelGGL((varlen_kernel<D, PAGED>),
-                     dim3(a.q_tiles, a.num_heads / a.heads_per_wg, a.batch), dim3(256), lds,
-                     stream, a);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int v = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 256);
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int D, bool PAGED>
+hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
+  const long long hg = a.num_heads / a.heads_per_wg;
+  const long long items = (long long)a.batch * a.q_tiles * hg;  // the full grid
+  if (a.batch <= kPersistMaxBatch && items < (1LL << 31)) {
+    const size_t lds = persist_list_offset<D>(PAGED) + kPersistListBytes;
+    const auto kernel = varlen_persistent_kernel<D, PAGED>;
+    hipError_t e = allow_lds(kernel, lds);
+    if (e != hipSuccess) return e;
+    long long grid = persistent_workgroups(kernel, lds);
+    if (grid > items) grid = items;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, stream, a);
+    return hipGetLastError();
+  }
+  const size_t lds = 4 * Geo<D>::TILEB + (PAGED ? kVarlenMaxTableEntries * sizeof(int) : 0);
+  const auto kernel = varlen_kernel<D, PAGED>;
+  hipError_t e = allow_lds(kernel, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3(a.q_tiles, (unsigned)hg, a.batch), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
