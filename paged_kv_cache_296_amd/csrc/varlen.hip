@@ -11,6 +11,9 @@
 //    waves of a workgroup share one kv head: with grouped heads they take up
 //    to 4 q heads of the group (same 32 rows), otherwise 4 consecutive row
 //    blocks of one head, so every K/V tile fetched is used by all 4 waves.
+//  * Up to 256 requests run in a persistent grid (two workgroups per CU) that
+//    walks a list of the work items every workgroup builds in LDS, requests
+//    ranked longest first; larger batches get one workgroup per item.
 //  * K and V stream through LDS in 64-key tiles, double buffered, moved from
 //    HBM straight into LDS by buffer loads with the LDS-destination bit (no
 //    register staging).  Both tiles are stored row-major, one 2*D-byte row
