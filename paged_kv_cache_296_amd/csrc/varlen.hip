@@ -328,7 +328,10 @@ __device__ __forceinline__ void pv(u32 vt, const u32* voff, const u32 (&pw)[2][8
 // true: keys are the first seqlens_k[b] tokens of sequence b in the paged
 // cache (block_table).  Every exit is uniform over the workgroup.
 template <int D, bool PAGED>
-__device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy, int b) {
+// cq = (cu_q[b], cu_q[b + 1]); ck = (cu_k[b], cu_k[b + 1]) (packed) or
+// (0, seqlens_k[b]) (paged), read by the caller.
+__device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy, int b,
+                                            int2 cq, int2 ck) {
   using G = Geo<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -339,21 +342,21 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
   const int h0 = hy * hpw;
   const int wg_rows = kWaveRows * rb;
 
-  const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
+  const int q0 = cq.x, q1 = cq.y;
   const int len_q = q1 - q0;
   const bool q_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && (b != 0 || q0 == 0) &&
                     (b != a.batch - 1 || q1 == a.total_q);
   int k0s = 0, len_k;
   unsigned err = 0;
   if constexpr (PAGED) {
-    len_k = a.seqlens_k[b];
+    len_k = ck.y;
     if (!q_ok) err = kErrCu;
     else if (len_k < 0 || (long long)len_k > (long long)a.max_blocks_per_seq * a.block_size)
       err = kErrSpan;
     else if (len_q > a.max_len_q || len_k > a.max_len_k) err = kErrMaxLen;
   } else {
-    k0s = a.cu_k[b];
-    const int k1s = a.cu_k[b + 1];
+    k0s = ck.x;
+    const int k1s = ck.y;
     len_k = k1s - k0s;
     const bool cu_ok = q_ok && k0s >= 0 && k1s >= k0s && k1s <= a.total_k &&
                        (b != 0 || k0s == 0) && (b != a.batch - 1 || k1s == a.total_k);
@@ -564,7 +567,10 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void varlen_kernel(VarlenArgs a) {
-  varlen_item<D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  const int b = blockIdx.z;
+  const int2 cq = make_int2(a.cu_q[b], a.cu_q[b + 1]);
+  const int2 ck = PAGED ? make_int2(0, a.seqlens_k[b]) : make_int2(a.cu_k[b], a.cu_k[b + 1]);
+  varlen_item<D, PAGED>(a, blockIdx.x, blockIdx.y, b, cq, ck);
 }
 
 // Persistent form for batches of up to kPersistMaxBatch requests: as many
@@ -580,7 +586,8 @@ template <int D>
 constexpr int persist_list_offset(bool paged) {
   return 4 * Geo<D>::TILEB + (paged ? kVarlenMaxTableEntries * (int)sizeof(int) : 0);
 }
-constexpr int kPersistListBytes = (4 * kPersistMaxBatch + 1) * (int)sizeof(int);
+// ord, pre, key, nqt, then copies of cu_q and of cu_k (or seqlens_k)
+constexpr int kPersistListBytes = (6 * kPersistMaxBatch + 3) * (int)sizeof(int);
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -590,10 +597,16 @@ void varlen_persistent_kernel(VarlenArgs a) {
   int* pre = ord + kPersistMaxBatch;        // [B + 1] items before rank r
   int* key = pre + kPersistMaxBatch + 1;    // key tiles, then scan scratch
   int* nqt = key + kPersistMaxBatch;        // q tiles of request b
+  int* lcq = nqt + kPersistMaxBatch;        // [B + 1] copy of cu_q
+  int* lck = lcq + kPersistMaxBatch + 1;    // [B + 1] copy of cu_k, or seqlens_k
   const int tid = threadIdx.x;
   const int B = a.batch;
   const int hpw = a.heads_per_wg, hg = a.num_heads / hpw;
   const int wg_rows = kWaveRows * (kWaves / hpw);
+  for (int i = tid; i <= B; i += 256) {
+    lcq[i] = a.cu_q[i];
+    lck[i] = PAGED ? (i < B ? a.seqlens_k[i] : 0) : a.cu_k[i];
+  }
   if (tid < B) {
     // the q tiles the full grid would give this request (at least one, so
     // that its lengths are checked); key tiles for the ranking only
@@ -645,7 +658,12 @@ void varlen_persistent_kernel(VarlenArgs a) {
     const int hy = __builtin_amdgcn_readfirstlane(rem / t);
     const int qt = __builtin_amdgcn_readfirstlane(rem - (rem / t) * t);
     __syncthreads();  // every wave is done with the previous item's tiles
-    varlen_item<D, PAGED>(a, qt, hy, b);
+    const int2 cq = make_int2(__builtin_amdgcn_readfirstlane(lcq[b]),
+                              __builtin_amdgcn_readfirstlane(lcq[b + 1]));
+    const int2 ck = PAGED ? make_int2(0, __builtin_amdgcn_readfirstlane(lck[b]))
+                          : make_int2(__builtin_amdgcn_readfirstlane(lck[b]),
+                                      __builtin_amdgcn_readfirstlane(lck[b + 1]));
+    varlen_item<D, PAGED>(a, qt, hy, b, cq, ck);
   }
 }
 
