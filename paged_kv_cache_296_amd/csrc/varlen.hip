@@ -577,7 +577,7 @@ void varlen_kernel(VarlenArgs a) {
 // workgroups as fit on the device, each building the same item list in LDS
 // -- only the q tiles a request has, requests ranked by key-tile count,
 // longest first -- and taking items k * G + w (k even) or k * G + G - 1 - w
-// (k odd) of it, so that every workgroup gets a similar mix of long and
+// (k odd) of it, w being the workgroup's slot in XCD-major order, so that every workgroup gets a similar mix of long and
 // short items and the list ends on the shortest ones.  Saves the launch and
 // request lookups of the empty and the per-tile workgroups and drains the
 // tail in order.
@@ -642,7 +642,12 @@ void varlen_persistent_kernel(VarlenArgs a) {
   if (tid == 0) pre[0] = 0;
   __syncthreads();
   const int total = pre[B];
-  const int G = gridDim.x, w = blockIdx.x;
+  // slot of this workgroup in XCD-major order: workgroups are dealt to the
+  // 8 XCDs round robin (w % 8), so neighbouring slots -- consecutive items
+  // of one request and head group, which read the same K/V tiles -- run on
+  // the same XCD and share its L2
+  const int G = gridDim.x;
+  const int w = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : blockIdx.x;
   for (int k = 0;; ++k) {
     const long long item = (long long)k * G + ((k & 1) ? G - 1 - w : w);
     if (item >= total) break;
