@@ -577,10 +577,10 @@ void varlen_kernel(VarlenArgs a) {
 // workgroups as fit on the device, each building the same item list in LDS
 // -- only the q tiles a request has, requests ranked by key-tile count,
 // longest first -- and taking items k * G + w (k even) or k * G + G - 1 - w
-// (k odd) of it, w being the workgroup's slot in XCD-major order, so that every workgroup gets a similar mix of long and
-// short items and the list ends on the shortest ones.  Saves the launch and
-// request lookups of the empty and the per-tile workgroups and drains the
-// tail in order.
+// (k odd) of it, w being the workgroup's slot in XCD-major order, so that
+// every workgroup gets a similar mix of long and short items and the list
+// ends on the shortest ones.  Saves the launch and request lookups of the
+// empty and the per-tile workgroups and drains the tail in order.
 constexpr int kPersistMaxBatch = 256;
 template <int D>
 constexpr int persist_list_offset(bool paged) {
