@@ -85,6 +85,28 @@ def test_decode_b256_long_sampled():
     torch.cuda.empty_cache()
 
 
+def test_mixed_step_decode_sampled():
+    """The decode half of the mixed continuous-batching step at full size and
+    in the launch the bench times (512 sequences, 16..8192 cached tokens, the
+    new token appended in place with a fresh block from the free list at block
+    boundaries, persistent kernel with runs): both pools bit for bit against
+    the oracle's append (every appended row, nothing else touched), and the
+    shortest, the longest, one block-boundary and six random sequences'
+    outputs against the oracle."""
+    case = workloads.make_config("mixed_step", device=DEV, part="decode")
+    L = case.lengths
+    order = np.argsort(L)
+    rng = np.random.default_rng(35)
+    seqs = set([int(order[0]), int(order[1]), int(order[-1]), int(order[-2])] +
+               rng.choice(len(L), 6, replace=False).tolist())
+    boundary = np.nonzero(L % 16 == 0)[0]
+    if len(boundary):
+        seqs.add(int(boundary[0]))
+    run_case(case, "bf16", seqs=np.array(sorted(seqs), dtype=np.int32), check_pool=True)
+    del case
+    torch.cuda.empty_cache()
+
+
 SMALL = []
 for dtype in ("bf16", "fp32"):
     for D in (64, 128):
