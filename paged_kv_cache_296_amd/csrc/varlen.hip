@@ -506,9 +506,8 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
     u32 pw[2][8];
     // the interleaved phase runs at raised wave priority, so that the other
     // wave on this SIMD fills in around it rather than competing for issue
-    // (3 % faster when the loop still summed with fp32 adds; with the
-    // current loop, priority 0, 1 or 3, or raising it from the max on, all
-    // measure within run-to-run noise)
+    // (without it, or with P.V raised instead: 7 % slower at head_dim 64,
+    // 2-3 % on short items at head_dim 128, the 16-request batch even)
     __builtin_amdgcn_s_setprio(1);
     qk_and_exp<D>(kofs(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
     __builtin_amdgcn_s_setprio(0);
