@@ -597,53 +597,68 @@ void varlen_kernel(VarlenArgs a) {
   varlen_item<D, PAGED>(a, blockIdx.x, blockIdx.y, b, cq, ck);
 }
 
-// Persistent form for batches of up to kPersistMaxBatch requests: as many
-// workgroups as fit on the device, each building the same item list in LDS
-// -- only the q tiles a request has, requests ranked by key-tile count,
-// longest first -- and taking items k * G + w (k even) or k * G + G - 1 - w
-// (k odd) of it, w being the workgroup's slot in XCD-major order, so that
-// every workgroup gets a similar mix of long and short items and the list
-// ends on the shortest ones.  Saves the launch and request lookups of the
-// empty and the per-tile workgroups and drains the tail in order.
-constexpr int kPersistMaxBatch = 256;
+// Persistent form for batches of up to kPersistMaxPacked (packed keys) or
+// kPersistMaxPaged (paged keys) requests: as many workgroups as fit on the
+// device, each building the same item list in LDS -- only the q tiles a
+// request has; up to kRankMaxBatch requests ranked by key-tile count,
+// longest first, larger batches in request order -- and taking items
+// k * G + w (k even) or k * G + G - 1 - w (k odd) of it, w being the
+// workgroup's slot in XCD-major order, so that every workgroup gets a
+// similar mix of long and short items and a ranked list ends on the
+// shortest ones.  Saves the launch and request lookups of the empty and the
+// per-tile workgroups and drains the tail in order.
+constexpr int kRankMaxBatch = 256;
+constexpr int kPersistMaxPacked = 960;
+constexpr int kPersistMaxPaged = 480;
 template <int D>
 constexpr int persist_list_offset(bool paged) {
   return 4 * Geo<D>::TILEB + (paged ? kVarlenMaxTableEntries * (int)sizeof(int) : 0);
 }
-// ord, pre, key, nqt, then copies of cu_q and of cu_k (or seqlens_k)
-constexpr int kPersistListBytes = (6 * kPersistMaxBatch + 3) * (int)sizeof(int);
+// pre[B + 1], nqt[B], copies of cu_q[B + 1] and of cu_k (or seqlens_k)
+// [B + 1], and ord[B] for a ranked batch; at most 80 KB per workgroup in all
+// (two per CU) at the batch limits
+constexpr int persist_list_bytes(int B) {
+  return (4 * B + 3 + (B <= kRankMaxBatch ? B : 0)) * (int)sizeof(int);
+}
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void varlen_persistent_kernel(VarlenArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* ord = reinterpret_cast<int*>(smem + persist_list_offset<D>(PAGED));  // rank -> request
-  int* pre = ord + kPersistMaxBatch;        // [B + 1] items before rank r
-  int* key = pre + kPersistMaxBatch + 1;    // key tiles, then scan scratch
-  int* nqt = key + kPersistMaxBatch;        // q tiles of request b
-  int* lcq = nqt + kPersistMaxBatch;        // [B + 1] copy of cu_q
-  int* lck = lcq + kPersistMaxBatch + 1;    // [B + 1] copy of cu_k, or seqlens_k
   const int tid = threadIdx.x;
   const int B = a.batch;
+  const bool ranked = B <= kRankMaxBatch;
+  int* pre = reinterpret_cast<int*>(smem + persist_list_offset<D>(PAGED));  // [B + 1] items before rank r
+  int* nqt = pre + B + 1;                   // q tiles of request b
+  int* lcq = nqt + B;                       // [B + 1] copy of cu_q
+  int* lck = lcq + B + 1;                   // [B + 1] copy of cu_k, or seqlens_k
+  int* ord = lck + B + 1;                   // rank -> request (ranked batches)
+  // scratch while the list is built: the tile buffers, idle until the
+  // first item (key tiles of up to kRankMaxBatch requests, then 256 partial
+  // sums of the scan)
+  int* key = reinterpret_cast<int*>(smem);
+  int* part = key + kRankMaxBatch;
   const int hpw = a.heads_per_wg, hg = a.num_heads / hpw;
   const int wg_rows = kWaveRows * (kWaves / hpw);
   for (int i = tid; i <= B; i += 256) {
     lcq[i] = a.cu_q[i];
     lck[i] = PAGED ? (i < B ? a.seqlens_k[i] : 0) : a.cu_k[i];
   }
-  if (tid < B) {
+  for (int i = tid; i < B; i += 256) {
     // the q tiles the full grid would give this request (at least one, so
     // that its lengths are checked); key tiles for the ranking only
-    long long lq = (long long)a.cu_q[tid + 1] - a.cu_q[tid];
+    long long lq = (long long)a.cu_q[i + 1] - a.cu_q[i];
     lq = lq < 0 ? 0 : (lq > (long long)a.q_tiles * wg_rows ? (long long)a.q_tiles * wg_rows : lq);
     const int t = (int)((lq + wg_rows - 1) / wg_rows);
-    nqt[tid] = t > 0 ? t : 1;
-    long long lk = PAGED ? (long long)a.seqlens_k[tid] : (long long)a.cu_k[tid + 1] - a.cu_k[tid];
-    lk = lk < 0 ? 0 : (lk > a.max_len_k ? a.max_len_k : lk);
-    key[tid] = (int)((lk + kKeys - 1) / kKeys);
+    nqt[i] = t > 0 ? t : 1;
+    if (ranked) {
+      long long lk = PAGED ? (long long)a.seqlens_k[i] : (long long)a.cu_k[i + 1] - a.cu_k[i];
+      lk = lk < 0 ? 0 : (lk > a.max_len_k ? a.max_len_k : lk);
+      key[i] = (int)((lk + kKeys - 1) / kKeys);
+    }
   }
   __syncthreads();
-  if (tid < B) {
+  if (ranked && tid < B) {
     const int kb = key[tid];
     int r = 0;
     for (int j = 0; j < B; ++j) {
@@ -653,16 +668,27 @@ void varlen_persistent_kernel(VarlenArgs a) {
     ord[r] = tid;
   }
   __syncthreads();
-  // inclusive scan of the items in rank order
-  key[tid] = tid < B ? nqt[ord[tid]] * hg : 0;
+  // prefix sums of the items in rank order: thread t takes ranks 4t .. 4t+3
+  // (B <= 1024), then a scan of the 256 partial sums
+  int run[4], acc_items = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 4 * tid + k;
+    acc_items += r < B ? nqt[ranked ? ord[r] : r] * hg : 0;
+    run[k] = acc_items;
+  }
+  part[tid] = acc_items;
   __syncthreads();
-  for (int off = 1; off < kPersistMaxBatch; off <<= 1) {
-    const int v = tid >= off ? key[tid - off] : 0;
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
-    key[tid] += v;
+    part[tid] += v;
     __syncthreads();
   }
-  if (tid < B) pre[tid + 1] = key[tid];
+  const int base_items = tid > 0 ? part[tid - 1] : 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (4 * tid + k < B) pre[4 * tid + k + 1] = base_items + run[k];
   if (tid == 0) pre[0] = 0;
   __syncthreads();
   const int total = pre[B];
@@ -681,7 +707,7 @@ void varlen_persistent_kernel(VarlenArgs a) {
       if (pre[mid] <= item) lo = mid;
       else hi = mid;
     }
-    const int b = __builtin_amdgcn_readfirstlane(ord[lo]);
+    const int b = __builtin_amdgcn_readfirstlane(ranked ? ord[lo] : lo);
     const int rem = (int)item - pre[lo];
     const int t = nqt[b];
     const int hy = __builtin_amdgcn_readfirstlane(rem / t);
@@ -734,8 +760,8 @@ template <int D, bool PAGED>
 hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
   const long long hg = a.num_heads / a.heads_per_wg;
   const long long items = (long long)a.batch * a.q_tiles * hg;  // the full grid
-  if (a.batch <= kPersistMaxBatch && items < (1LL << 31)) {
-    const size_t lds = persist_list_offset<D>(PAGED) + kPersistListBytes;
+  if (a.batch <= (PAGED ? kPersistMaxPaged : kPersistMaxPacked) && items < (1LL << 31)) {
+    const size_t lds = persist_list_offset<D>(PAGED) + persist_list_bytes(a.batch);
     const auto kernel = varlen_persistent_kernel<D, PAGED>;
     hipError_t e = allow_lds(kernel, lds);
     if (e != hipSuccess) return e;

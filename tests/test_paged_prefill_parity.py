@@ -161,9 +161,11 @@ def test_varlen_paged_small_ragged(D, group, bs):
     _paged_run(pc)
 
 
-def test_varlen_paged_large_batch_grid_form():
-    """280 requests (above the persistent kernel's 256): the grid form."""
-    pc = workloads.make_paged_prefill(seed=3550, dtype="bf16", batch=280, num_heads=8,
+@pytest.mark.parametrize("batch", [280, 500])
+def test_varlen_paged_large_batches(batch):
+    """280 requests: the persistent kernel without the longest-first ranking;
+    500 (above its 480 for paged keys): the grid form."""
+    pc = workloads.make_paged_prefill(seed=3550 + batch, dtype="bf16", batch=batch, num_heads=8,
                                       num_kv_heads=2, head_dim=128, q_lengths=("uniform", 0, 40),
                                       prefix=("uniform", 0, 60), device=DEV)
     _paged_run(pc)

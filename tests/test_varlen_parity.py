@@ -5,9 +5,10 @@ key, one with seven), the 16-sequence prefill batch at full size (sampled
 rows for the oracle), the 8 x 1024 prefill of the mixed step, and small cases
 with ragged tails, empty requests, head_dim 64/128, group sizes 1..8 (each
 workgroup packing of q heads), negative / zero / large softmax scales and
-scores whose row max keeps moving across key tiles; batches above and below
-the 256-request limit of the persistent kernel (the grid form serves larger
-batches), and bit-identical results from the two forms.
+scores whose row max keeps moving across key tiles; batches on both sides of
+the persistent kernel's limits (256 requests ranked longest first, 960 in
+all; the grid form serves larger batches), and bit-identical results across
+those boundaries.
 """
 import numpy as np
 import pytest
@@ -153,29 +154,33 @@ def test_empty():
     assert out.shape == q.shape
 
 
-def test_large_batch_grid_form():
-    """300 requests: more than the persistent kernel takes, so the one-
-    workgroup-per-tile grid serves them; ragged lengths with empty requests."""
-    case = workloads.make_varlen(seed=4600, dtype="bf16", batch=300, num_heads=8, num_kv_heads=2,
-                                 head_dim=128, q_lengths=("uniform", 0, 40),
+@pytest.mark.parametrize("batch", [300, 1000])
+def test_large_batches(batch):
+    """300 requests: the persistent kernel without the longest-first ranking;
+    1000: more than it takes, so the one-workgroup-per-tile grid serves them.
+    Ragged lengths with empty requests."""
+    case = workloads.make_varlen(seed=4600 + batch, dtype="bf16", batch=batch, num_heads=8,
+                                 num_kv_heads=2, head_dim=128, q_lengths=("uniform", 0, 40),
                                  k_lengths=("uniform", 0, 100), device=DEV)
     run_case(case)
 
 
-def test_persistent_and_grid_forms_agree_bitwise():
-    """The first 256 requests run through the persistent kernel on their own
-    and through the grid form inside a 257-request batch: same bits (each
-    item runs the same arithmetic whichever form schedules it)."""
-    big = workloads.make_varlen(seed=4700, dtype="bf16", batch=257, num_heads=8, num_kv_heads=2,
-                                head_dim=128, q_lengths=("uniform", 0, 70),
+@pytest.mark.parametrize("n", [256, 960])
+def test_schedules_agree_bitwise(n):
+    """The first n requests of an (n + 1)-request batch run on their own and
+    inside the whole batch: at n = 256 the ranked and the unranked persistent
+    schedules, at n = 960 the persistent kernel and the grid form.  Same bits
+    (each item runs the same arithmetic whichever schedule places it)."""
+    big = workloads.make_varlen(seed=4700 + n, dtype="bf16", batch=n + 1, num_heads=8,
+                                num_kv_heads=2, head_dim=128, q_lengths=("uniform", 0, 70),
                                 k_lengths=("uniform", 0, 150), device=DEV)
-    nq = int(big.cu_seq_lens_q[256])
-    nk = int(big.cu_seq_lens_k[256])
+    nq = int(big.cu_seq_lens_q[n])
+    nk = int(big.cu_seq_lens_k[n])
     args_big = (big.q, big.k, big.v, big.cu_seq_lens_q, big.cu_seq_lens_k, big.max_length_q,
                 big.max_length_k)
     out_big = pkv.varlen(*args_big, softmax_scale=big.softmax_scale)
     small = (big.q[:, :nq].contiguous(), big.k[:, :nk].contiguous(), big.v[:, :nk].contiguous(),
-             big.cu_seq_lens_q[:257].contiguous(), big.cu_seq_lens_k[:257].contiguous(),
+             big.cu_seq_lens_q[:n + 1].contiguous(), big.cu_seq_lens_k[:n + 1].contiguous(),
              big.max_length_q, big.max_length_k)
     out_small = pkv.varlen(*small, softmax_scale=big.softmax_scale)
     torch.cuda.synchronize()
