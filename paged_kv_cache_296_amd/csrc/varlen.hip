@@ -736,15 +736,16 @@ hipError_t allow_lds(K kernel, size_t lds) {
 }
 
 // Workgroups of the persistent kernel that fit on the device at once
-// (launch geometry only), per device.
+// (launch geometry only), per device; the dynamic LDS size varies with the
+// batch, so the cached value is kept with the size it was taken for.
 template <class K>
 int persistent_workgroups(K kernel, size_t lds) {
-  static std::atomic<int> cache[64];
+  static std::atomic<unsigned long long> cache[64];  // lds << 32 | workgroups
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (dev >= 0 && dev < 64) {
-    const int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
+    const unsigned long long c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0 && (c >> 32) == lds) return (int)(c & 0xffffffffu);
   }
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess)
@@ -752,7 +753,8 @@ int persistent_workgroups(K kernel, size_t lds) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const int v = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 256);
-  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  if (dev >= 0 && dev < 64)
+    cache[dev].store(((unsigned long long)lds << 32) | (unsigned)v, std::memory_order_relaxed);
   return v;
 }
 
