@@ -185,3 +185,16 @@ def test_schedules_agree_bitwise(n):
     out_small = pkv.varlen(*small, softmax_scale=big.softmax_scale)
     torch.cuda.synchronize()
     assert torch.equal(out_small[0], out_big[0, :nq])
+
+
+def test_repeated_calls_bitwise():
+    """The persistent schedule is static (no atomics, no timing-dependent
+    order): the prefill batch gives the same bits on every call."""
+    case = workloads.make_config("varlen_prefill", device=DEV)
+    args = (case.q, case.k, case.v, case.cu_seq_lens_q, case.cu_seq_lens_k, case.max_length_q,
+            case.max_length_k)
+    first = pkv.varlen(*args, softmax_scale=case.softmax_scale)
+    for _ in range(3):
+        again = pkv.varlen(*args, softmax_scale=case.softmax_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
