@@ -7,13 +7,14 @@
 // sequence b and is copied, bit for bit, to slot p mod block_size of
 // physical block block_table[b][p / block_size], for K and for V.
 //
-// How: one wave per 4 consecutive packed rows.  Everything that locates a
+// How: one wave per 2 consecutive packed rows.  Everything that locates a
 // row -- its request (one load of cu per lane and a ballot, or a binary
 // search for large batches), its token position, its table entry -- is
 // wave-uniform and runs on the scalar unit; the 64 lanes then move the rows'
 // Hkv * D elements (2 KB per row of K at 8 kv heads x 128 bf16) in 16-byte
-// pieces, issuing the loads of all 4 rows of K and V before any store, so
-// each lane has 16 loads in flight.  A row is contiguous at both ends (a
+// pieces, issuing the loads of both rows of K and V before any store, so
+// each lane has 8 loads in flight (1, 2, 4 and 8 rows per wave measured
+// 40.2, 39.4, 40.8 and 52 us on the 16-request prefill batch).  A row is contiguous at both ends (a
 // token row of the cache is [Hkv][D] like a packed row), so both sides are
 // coalesced.  The packed rows are read once, with the non-temporal hint
 // (measured 28 % faster than plain loads on the 16-request prefill batch:
@@ -30,7 +31,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWavesPerGroup = 4;
-constexpr int kRowsPerWave = 4;   // rows one wave copies, all loads in flight together
+constexpr int kRowsPerWave = 2;   // rows one wave copies, all loads in flight together
 constexpr int kMaxPieces = 4;     // 16-byte pieces per lane per row (row_bytes <= 4 KB)
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u, kErrCu = 4u;
 
