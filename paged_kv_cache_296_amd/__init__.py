@@ -139,6 +139,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(stream, *args, **kw):
+    """torch.empty on the stream the kernels will run on: the caching
+    allocator then hands the block out again only to work ordered after them
+    on that stream, even once the caller has dropped it."""
+    if stream is None:
+        return torch.empty(*args, **kw)
+    with torch.cuda.stream(stream):
+        return torch.empty(*args, **kw)
+
+
 def check_decode_args(dtype, has_new, batch, num_heads, num_kv_heads, head_dim, num_blocks,
                       block_size, max_blocks_per_seq, partition_tokens=0) -> int:
     return _load().pkv_check_decode_args(int(dtype), int(has_new), batch, num_heads, num_kv_heads,
@@ -233,14 +243,14 @@ def _decode_call(fname, q, k_cache, v_cache, block_table, cache_seqlens, k_new, 
     if rc:
         raise PkvError(rc, "pkv_decode arguments")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(stream, q.shape, dtype=q.dtype, device=q.device)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q's shape and dtype")
     need = lib.pkv_decode_workspace_bytes(B, Hq, Hkv, D, bs, maxb, int(partition_tokens))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         if fname == "pkv_decode_merge":
             raise ValueError("decode_merge needs the workspace decode_partials filled")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(stream, need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = getattr(lib, fname)(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                         _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new), _ptr(out), B, Hq, Hkv, D,
@@ -279,7 +289,7 @@ def varlen(q, k, v, cu_seq_lens_q, cu_seq_lens_k, max_length_q, max_length_k, *,
     if rc:
         raise PkvError(rc, "pkv_varlen arguments")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(stream, q.shape, dtype=q.dtype, device=q.device)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q's shape and dtype")
     rc = lib.pkv_varlen(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k),
@@ -379,7 +389,7 @@ def varlen_paged(q, k_cache, v_cache, block_table, cu_seq_lens_q, seqlens_k, max
     if rc:
         raise PkvError(rc, "pkv_varlen_paged arguments")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(stream, q.shape, dtype=q.dtype, device=q.device)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q's shape and dtype")
     rc = lib.pkv_varlen_paged(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),

@@ -838,10 +838,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   store4(o * inv);
 }
 
-// Workgroups of the persistent kernel that fit on the device at once; queried
-// once per device and kernel (launch geometry only, no other state).
-template <class Kernel>
-int resident_workgroups(Kernel kernel, int threads) {
+// Workgroups of decode_partial_kernel<BF16, D, BS> that fit on the device at
+// once (launch geometry only, no other state).  Queried once per device and
+// instantiation: the instantiations differ in register use (two waves per
+// SIMD for bf16 at head_dim 128, three at 64, one for fp32 at 128), and every
+// one of them has the same function type, so the cache is keyed by the
+// template arguments, not by the kernel's type.
+template <bool BF16, int D, int BS>
+int resident_workgroups() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -850,7 +854,9 @@ int resident_workgroups(Kernel kernel, int threads) {
     if (v > 0) return v;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_kernel<BF16, D, BS>,
+                                                   kWaves * 64, 0) != hipSuccess)
+    per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
   const int v = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 256);
   if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
@@ -861,7 +867,7 @@ template <bool BF16, int D, int BS>
 hipError_t launch_one(const DecodeArgs& args, int phases, hipStream_t stream) {
   DecodeArgs a = args;
   const auto kernel = decode_partial_kernel<BF16, D, BS>;
-  long long wgs = resident_workgroups(kernel, kWaves * 64);
+  long long wgs = resident_workgroups<BF16, D, BS>();
   a.resident_waves = (int)(wgs * kWaves);
   // few units (up to two grid slots per resident wave): the direct grid;
   // more: the persistent kernel with runs

@@ -111,6 +111,19 @@ size_t workspace_for(const DecodePlan& p, int batch, int num_heads, int head_dim
 
 }  // namespace
 
+namespace pkv {
+
+// Workgroup shape of the varlen kernels: 4 waves of 32 query rows share one
+// kv head, taking up to 4 q heads of its group for the same rows (else
+// several 32-row blocks of one head).
+int varlen_heads_per_workgroup(int group) {
+  return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
+int varlen_rows_per_workgroup(int group) { return 32 * (4 / varlen_heads_per_workgroup(group)); }
+
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_status_string(int status) {

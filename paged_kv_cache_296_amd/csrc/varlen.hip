@@ -722,24 +722,39 @@ void varlen_persistent_kernel(VarlenArgs a) {
   }
 }
 
-// Dynamic LDS above 64 KB must be allowed once per device and kernel.
-template <class K>
-hipError_t allow_lds(K kernel, size_t lds) {
+// Dynamic LDS above 64 KB must be allowed per kernel.  Each instantiation
+// allows, once per device, the most it can ever request (the persistent form
+// at its batch limit), so later launches with larger lists are covered too.
+// Keyed by the template arguments: all four kernels of a form share one
+// function type.
+template <int D, bool PAGED, bool PERSIST>
+hipError_t allow_lds() {
   static std::atomic<bool> done[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  size_t lds;
+  const void* kernel;
+  if constexpr (PERSIST) {
+    lds = persist_list_offset<D>(PAGED) +
+          persist_list_bytes(PAGED ? kPersistMaxPaged : kPersistMaxPacked);
+    kernel = (const void*)varlen_persistent_kernel<D, PAGED>;
+  } else {
+    lds = 4 * Geo<D>::TILEB + (PAGED ? kVarlenMaxTableEntries * sizeof(int) : 0);
+    kernel = (const void*)varlen_kernel<D, PAGED>;
+  }
   const hipError_t e =
-      hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e == hipSuccess && dev >= 0 && dev < 64) done[dev].store(true, std::memory_order_release);
   return e;
 }
 
-// Workgroups of the persistent kernel that fit on the device at once
-// (launch geometry only), per device; the dynamic LDS size varies with the
-// batch, so the cached value is kept with the size it was taken for.
-template <class K>
-int persistent_workgroups(K kernel, size_t lds) {
+// Workgroups of varlen_persistent_kernel<D, PAGED> that fit on the device at
+// once (launch geometry only), per device and instantiation; the dynamic LDS
+// size varies with the batch, so the cached value is kept with the size it
+// was taken for.
+template <int D, bool PAGED>
+int persistent_workgroups(size_t lds) {
   static std::atomic<unsigned long long> cache[64];  // lds << 32 | workgroups
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -748,7 +763,8 @@ int persistent_workgroups(K kernel, size_t lds) {
     if (c != 0 && (c >> 32) == lds) return (int)(c & 0xffffffffu);
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, varlen_persistent_kernel<D, PAGED>,
+                                                   256, lds) != hipSuccess)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
@@ -764,31 +780,23 @@ hipError_t launch_v(const VarlenArgs& a, hipStream_t stream) {
   const long long items = (long long)a.batch * a.q_tiles * hg;  // the full grid
   if (a.batch <= (PAGED ? kPersistMaxPaged : kPersistMaxPacked) && items < (1LL << 31)) {
     const size_t lds = persist_list_offset<D>(PAGED) + persist_list_bytes(a.batch);
-    const auto kernel = varlen_persistent_kernel<D, PAGED>;
-    hipError_t e = allow_lds(kernel, lds);
+    hipError_t e = allow_lds<D, PAGED, true>();
     if (e != hipSuccess) return e;
-    long long grid = persistent_workgroups(kernel, lds);
+    long long grid = persistent_workgroups<D, PAGED>(lds);
     if (grid > items) grid = items;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((varlen_persistent_kernel<D, PAGED>), dim3((unsigned)grid), dim3(256), lds,
+                       stream, a);
     return hipGetLastError();
   }
   const size_t lds = 4 * Geo<D>::TILEB + (PAGED ? kVarlenMaxTableEntries * sizeof(int) : 0);
-  const auto kernel = varlen_kernel<D, PAGED>;
-  hipError_t e = allow_lds(kernel, lds);
+  hipError_t e = allow_lds<D, PAGED, false>();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kernel, dim3(a.q_tiles, (unsigned)hg, a.batch), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((varlen_kernel<D, PAGED>), dim3(a.q_tiles, (unsigned)hg, a.batch), dim3(256),
+                     lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
-
-int varlen_heads_per_workgroup(int group) {
-  return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-}
-
-int varlen_rows_per_workgroup(int group) {
-  return kWaveRows * (kWaves / varlen_heads_per_workgroup(group));
-}
 
 hipError_t launch_varlen(int dtype, int head_dim, const VarlenArgs& a, hipStream_t stream) {
   if (dtype != 1) return hipErrorInvalidValue;

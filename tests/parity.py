@@ -40,3 +40,16 @@ def assert_close(gpu, ref, dtype, what=""):
     ok, rep = compare(gpu, ref, dtype)
     assert ok, f"{what} parity failed: {rep}"
     return rep
+
+
+def tile_rows(cu_q, tile=32, every=8):
+    """Rows for the oracle: every `every`-th row of each request, plus both
+    edges of each of its `tile`-row q tiles (the rows one wave owns), plus
+    its last row."""
+    rows = []
+    for b in range(len(cu_q) - 1):
+        lo, hi = int(cu_q[b]), int(cu_q[b + 1])
+        r = np.arange(hi - lo)
+        keep = (r % every == 0) | (r % tile == 0) | (r % tile == tile - 1) | (r == hi - lo - 1)
+        rows += (lo + r[keep]).tolist()
+    return np.array(rows, dtype=np.int32)

@@ -14,7 +14,7 @@ import torch
 import oracle
 import paged_kv_cache_296_amd as pkv
 import workloads
-from tests.parity import assert_close, gpu_to_f64
+from tests.parity import assert_close, gpu_to_f64, tile_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -198,20 +198,14 @@ def test_varlen_paged_equals_packed_bitwise():
 def test_prefill_step_write_then_attend_full_size():
     """The 16-sequence prefill batch as a paged step: new rows written after
     each cached prefix, then attention over prefix + new through the table;
-    sampled rows against the oracle."""
+    every 8th row of each request and both edges of every q tile against the
+    oracle."""
     c = dict(workloads.CONFIGS["varlen_prefill"])
     c.pop("kind")
     pc = workloads.make_paged_prefill(device=DEV, **c)
     pkv.cache_write(pc.k_new, pc.v_new, pc.cu_seq_lens_q, pc.start, pc.k_cache, pc.v_cache,
                     pc.block_table)
-    rng = np.random.default_rng(37)
-    cq = pc.cu_seq_lens_q.cpu().numpy()
-    rows = []
-    for b in range(len(cq) - 1):
-        lo, hi = int(cq[b]), int(cq[b + 1])
-        if hi > lo:
-            rows += [lo, hi - 1] + rng.integers(lo, hi, size=2).tolist()
-    _paged_run(pc, rows=np.array(sorted(set(rows)), dtype=np.int32))
+    _paged_run(pc, rows=tile_rows(pc.cu_seq_lens_q.cpu().numpy()))
 
 
 def test_varlen_paged_bad_inputs_flag_and_poison():

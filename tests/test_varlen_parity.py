@@ -1,8 +1,8 @@
 """GPU parity of pkv_varlen against the fp64 oracle, on the same seeded bytes.
 
 Covers the HF page's worked example (a request with no key, one with a single
-key, one with seven), the 16-sequence prefill batch at full size (sampled
-rows for the oracle), the 8 x 1024 prefill of the mixed step, and small cases
+key, one with seven), the 16-sequence prefill batch at full size (every 8th row
+of each request and both edges of every q tile for the oracle), the 8 x 1024 prefill of the mixed step, and small cases
 with ragged tails, empty requests, head_dim 64/128, group sizes 1..8 (each
 workgroup packing of q heads), negative / zero / large softmax scales and
 scores whose row max keeps moving across key tiles; batches on both sides of
@@ -17,7 +17,7 @@ import torch
 import oracle
 import paged_kv_cache_296_amd as pkv
 import workloads
-from tests.parity import assert_close, gpu_to_f64
+from tests.parity import assert_close, gpu_to_f64, tile_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -58,21 +58,18 @@ def test_hf_example(golden):
             assert torch.equal(o[r, h].view(torch.int16), case.v[0, 0, h // 4].view(torch.int16))
 
 
-def test_prefill_full_sampled():
+def test_prefill_full_rows():
+    """The 16-request prefill batch at full size; the oracle takes every 8th
+    row of each request and both edge rows of every 32-row q tile."""
     case = workloads.make_config("varlen_prefill", device=DEV)
-    cq = case.cu_seq_lens_q.cpu().numpy()
-    rng = np.random.default_rng(44)
-    rows = []
-    for b in range(len(cq) - 1):
-        lo, hi = int(cq[b]), int(cq[b + 1])
-        if hi > lo:
-            rows += [lo, hi - 1] + rng.integers(lo, hi, size=3).tolist()
-    run_case(case, rows=np.array(sorted(set(rows)), dtype=np.int32))
+    rows = tile_rows(case.cu_seq_lens_q.cpu().numpy())
+    _, rep = run_case(case, rows=rows)
+    assert rep["rows"] == len(rows) * 32
 
 
-def test_mixed_step_prefill_sampled():
+def test_mixed_step_prefill_rows():
     case = workloads.make_config("mixed_step", device=DEV, part="prefill")
-    rows = np.arange(0, 8192, 97, dtype=np.int32)
+    rows = tile_rows(case.cu_seq_lens_q.cpu().numpy())
     run_case(case, rows=rows)
 
 
