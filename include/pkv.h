@@ -192,6 +192,35 @@ int pkv_decode_merge(int dtype, const void* q, void* k_cache, void* v_cache,
                      int32_t* err_flag, void* stream);
 
 /*
+ * pkv_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as pkv_decode without the workspace, which is
+ * instead a static array of PKV_DECODE_NOALLOC_SCRATCH_BYTES per GPU inside
+ * the library (reserved on every GPU the library runs on until the process
+ * ends).  No hipMalloc, hipFree or other allocation happens in the call; the
+ * first call on a device looks the array's address up once.
+ *
+ *  - Returns PKV_EWORKSPACE, enqueuing nothing, when pkv_decode_workspace_bytes
+ *    for these arguments exceeds PKV_DECODE_NOALLOC_SCRATCH_BYTES (a longer
+ *    partition_tokens needs less: e.g. 512 sequences x 32 heads x 8208 tokens
+ *    fit with 2048-token partitions); PKV_EINVAL when `stream` belongs to a
+ *    device other than the current one.
+ *  - Every call on one GPU uses the same array: calls that may overlap in
+ *    time on one GPU (different streams, different host threads) race and
+ *    must be serialised by the caller.  Calls on one stream are ordered and
+ *    safe.  The array needs no initialisation; each call's kernels write
+ *    whatever they later read.
+ */
+#define PKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pkv_decode_noalloc(int dtype, const void* q, void* k_cache, void* v_cache,
+                       const int32_t* block_table, const int32_t* cache_seqlens,
+                       const void* k_new, const void* v_new, void* out,
+                       int batch, int num_heads, int num_kv_heads, int head_dim,
+                       int num_blocks, int block_size, int max_blocks_per_seq,
+                       float softmax_scale, int partition_tokens,
+                       int32_t* err_flag, void* stream);
+
+/*
  * Host-only validation of pkv_varlen's scalar arguments.  Supported: bf16;
  * head_dim 64 or 128; num_heads a multiple of num_kv_heads.
  */

@@ -21,7 +21,8 @@ __all__ = [
     "varlen_paged", "decode_workspace_bytes", "decode_partition_tokens", "check_decode_args",
     "check_varlen_args", "check_cache_write_args", "check_varlen_paged_args", "status_string",
     "abi_version", "lib_path", "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
-    "BlockManager", "OutOfBlocks", "copy_blocks",
+    "BlockManager", "OutOfBlocks", "copy_blocks", "decode_noalloc",
+    "DECODE_NOALLOC_SCRATCH_BYTES",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENOMEM = 0, 1, 2, 3, 4, 5
@@ -62,6 +63,9 @@ def _load():
             fn = getattr(L, name)
             fn.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, SZ, P, P]
             fn.restype = I
+        L.pkv_decode_noalloc.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P,
+                                         P]
+        L.pkv_decode_noalloc.restype = I
         L.pkv_check_varlen_args.argtypes = [I] * 9
         L.pkv_check_varlen_args.restype = I
         L.pkv_varlen.argtypes = [I, P, P, P, P, P, I, I, P, I, I, I, I, I, I, F, P, P]
@@ -259,6 +263,39 @@ def _decode_call(fname, q, k_cache, v_cache, block_table, cache_seqlens, k_new, 
     if rc:
         raise PkvError(rc, fname)
     return out, workspace
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None, *,
+                   out, softmax_scale=None, partition_tokens=0, err_flag=None, stream=None):
+    """pkv_decode_noalloc: decode with the library's static per-GPU scratch
+    instead of a workspace, for callers that cannot allocate (graph capture).
+    `out` is required; nothing is allocated.  Calls that overlap in time on
+    one GPU share the scratch and race.  Returns out."""
+    lib = _load()
+    if out is None:
+        raise ValueError("decode_noalloc allocates nothing: pass out")
+    _need_gpu(q, k_cache, v_cache, block_table, cache_seqlens, k_new, v_new, out, err_flag)
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                 cache_seqlens=cache_seqlens, k_new=k_new, v_new=v_new, out=out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q [B, 1, Hq, D], caches [num_blocks, bs, Hkv, D], table [B, max_blocks]")
+    B, _, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rc = lib.pkv_decode_noalloc(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_table), _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new),
+                                _ptr(out), B, Hq, Hkv, D, NB, bs, block_table.shape[1],
+                                float(softmax_scale), int(partition_tokens), _ptr(err_flag),
+                                _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_decode_noalloc")
+    return out
 
 
 def varlen(q, k, v, cu_seq_lens_q, cu_seq_lens_k, max_length_q, max_length_k, *,

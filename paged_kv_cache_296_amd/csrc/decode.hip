@@ -902,7 +902,30 @@ hipError_t launch_one(const DecodeArgs& args, int phases, hipStream_t stream) {
   return hipSuccess;
 }
 
+// Workspace of pkv_decode_noalloc: one array per GPU, part of this code
+// object, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host that name is only a stand-in); it looks up
+// the device address once per device and passes that.
+__device__ __align__(256) char scratch[kDecodeScratchBytes];
+
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeArgs& a,
                          int phases, hipStream_t stream) {

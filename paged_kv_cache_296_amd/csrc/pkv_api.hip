@@ -12,7 +12,7 @@
 namespace {
 
 constexpr int kMaxPartitionBlocks = 256;  // LDS table slice per wave
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool decode_shape_ok(int head_dim, int block_size) {
   return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
@@ -171,7 +171,10 @@ size_t pkv_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, in
 
 namespace {
 
-int decode_impl(int phases, int dtype, const void* q, void* k_cache, void* v_cache,
+// own_scratch: the library's static decode scratch replaces the caller's
+// workspace (pkv_decode_noalloc).
+int decode_impl(int phases, bool own_scratch, int dtype, const void* q, void* k_cache,
+                void* v_cache,
                 const int32_t* block_table, const int32_t* cache_seqlens,
                 const void* k_new, const void* v_new, void* out,
                 int batch, int num_heads, int num_kv_heads, int head_dim,
@@ -190,6 +193,19 @@ int decode_impl(int phases, int dtype, const void* q, void* k_cache, void* v_cac
   DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
                              partition_tokens);
   const size_t need = workspace_for(p, batch, num_heads, head_dim);
+  if (own_scratch) {
+    if (need > pkv::kDecodeScratchBytes) return PKV_EWORKSPACE;
+    // the scratch address is per device: the launch must go to the current one
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_EHIP;
+    if (stream != nullptr) {
+      hipDevice_t sdev = -1;
+      if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return PKV_EHIP;
+      if (sdev != dev) return PKV_EINVAL;
+    }
+    if (pkv::decode_scratch(&workspace) != hipSuccess) return PKV_EHIP;
+    workspace_bytes = pkv::kDecodeScratchBytes;
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_EWORKSPACE;
 
   pkv::DecodeArgs a;
@@ -245,9 +261,21 @@ extern "C" {
       num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,       \
       softmax_scale, partition_tokens, workspace, workspace_bytes, err_flag, stream
 
-int pkv_decode(PKV_DECODE_ARGS) { return decode_impl(3, PKV_DECODE_FWD); }
-int pkv_decode_partials(PKV_DECODE_ARGS) { return decode_impl(1, PKV_DECODE_FWD); }
-int pkv_decode_merge(PKV_DECODE_ARGS) { return decode_impl(2, PKV_DECODE_FWD); }
+int pkv_decode(PKV_DECODE_ARGS) { return decode_impl(3, false, PKV_DECODE_FWD); }
+int pkv_decode_partials(PKV_DECODE_ARGS) { return decode_impl(1, false, PKV_DECODE_FWD); }
+int pkv_decode_merge(PKV_DECODE_ARGS) { return decode_impl(2, false, PKV_DECODE_FWD); }
+
+int pkv_decode_noalloc(int dtype, const void* q, void* k_cache, void* v_cache,
+                       const int32_t* block_table, const int32_t* cache_seqlens,
+                       const void* k_new, const void* v_new, void* out, int batch,
+                       int num_heads, int num_kv_heads, int head_dim, int num_blocks,
+                       int block_size, int max_blocks_per_seq, float softmax_scale,
+                       int partition_tokens, int32_t* err_flag, void* stream) {
+  return decode_impl(3, true, dtype, q, k_cache, v_cache, block_table, cache_seqlens, k_new,
+                     v_new, out, batch, num_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, softmax_scale, partition_tokens, nullptr, 0, err_flag,
+                     stream);
+}
 
 int pkv_check_varlen_args(int dtype, int batch, int total_q, int total_k, int num_heads,
                           int num_kv_heads, int head_dim, int max_length_q, int max_length_k) {

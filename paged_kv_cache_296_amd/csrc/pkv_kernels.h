@@ -88,6 +88,11 @@ struct CopyBlocksArgs {
   long long block_bytes;  // block_size * num_kv_heads * head_dim * element size
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+// The library's own decode workspace for callers that cannot allocate: its
+// size, and its device address on the current device (looked up once per
+// device, then cached).
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** ptr);
 // Table entries one paged-varlen workgroup stages in LDS (bounds max_length_k).
 constexpr int kVarlenMaxTableEntries = 2048;
 // Workgroup shape of the varlen kernel for a q-heads-per-kv-head ratio.

@@ -81,7 +81,22 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t) {
   EXPECT(a.block_bytes % 16 == 0 && a.n > 0);
   return hipSuccess;
 }
+// the static scratch of pkv_decode_noalloc: the same stand-in address
+hipError_t decode_scratch(void** ptr) {
+  *ptr = (void*)kWs;
+  return hipSuccess;
+}
 }  // namespace pkv
+
+// the two runtime queries pkv_decode_noalloc makes: device 0 for everything
+hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
 
 // a stand-in for device pointers: the host code never dereferences them
 static void* const kFake = (void*)(uintptr_t)0x100000;
@@ -114,6 +129,19 @@ static void decode_plans() {
                                        nullptr);
               EXPECT(r == PKV_OK || r == PKV_EUNSUPPORTED);
               EXPECT(B == 0 || r != PKV_OK || g_launches == before + 1);
+              // the no-alloc form: the library's scratch, or a refusal when the
+              // workspace would not fit in it
+              g_ws_bytes = pkv::kDecodeScratchBytes;
+              const int before_na = g_launches;
+              const int rn = pkv_decode_noalloc(PKV_BF16, kFake, kFake, kFake,
+                                                (const int32_t*)kFake, (const int32_t*)kFake,
+                                                kFake, kFake, kFake, B, h[0], h[1], D, 1000, bs,
+                                                mb, 0.1f, pt, nullptr, nullptr);
+              if (need > pkv::kDecodeScratchBytes)
+                EXPECT(B == 0 ? rn == PKV_OK : (rn == PKV_EWORKSPACE && g_launches == before_na));
+              else
+                EXPECT(rn == r && (B == 0 || r != PKV_OK || g_launches == before_na + 1));
+              g_ws_bytes = need;
               // one byte short of the workspace is refused before any launch
               if (need > 1) {
                 const int r2 = pkv_decode_partials(PKV_BF16, kFake, kFake, kFake,
