@@ -2,34 +2,45 @@
 """Throughput of the paged-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--placement permuted|contiguous]
 
 A step is one pass of paged decode over the batch of the chosen workload
 (default: the long-context batch -- 256 sequences, 64 q / 8 kv heads,
 head_dim 128, 16-token blocks, log-uniform 1k..32k cached tokens, 512-token
-split-context partitions): the per-partition kernel (block-table gather,
-QK^T, online softmax, P.V) then the (m, l) merge.  Inputs are resident in HBM
-before timing starts.  W untimed steps, then exactly K timed steps between two
-device synchronisations; `value` is KV bytes read per second (algorithmic:
-every cached K and V element of each kv head counted once).
+split-context partitions): the plan kernel, the per-partition kernel
+(block-table gather, QK^T, online softmax, P.V) and the (m, l) merge.  Inputs
+are resident in HBM before timing starts.  W untimed steps, then exactly K
+timed steps; before each timed step the 256 MB last-level cache is flushed
+(a 1 GiB buffer is overwritten, outside the timed interval), and each step is
+timed by HIP events recorded on the launch stream around it.  `value` is KV
+bytes read per second (algorithmic: every cached K and V element of each kv
+head counted once) over the mean cold step time.
 
 The same JSON line carries
-  roofline      the per-partition kernel against the 8 TB/s HBM peak, its
-                duration taken from HIP events recorded on the launch stream
-                around each launch in the timed region;
-  cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
-                same workload (about --cpu-seconds of work);
-  prefill       the 16-sequence varlen prefill batch: algorithmic TFLOP/s
-                against the 2.5 PFLOP/s dense bf16 MFMA peak;
-  paged_prefill the same batch as a paged step: cache write of the new rows,
-                then varlen attention through the block table;
-  mixed_step    the continuous-batching step: 512 decode sequences with the
-                in-place append, then 8 x 1024 prefill tokens, on one stream.
+  roofline        the per-partition kernel against the 8 TB/s HBM peak, its
+                  duration taken from HIP events around each launch in the
+                  timed region, and against the measured streaming-read
+                  ceiling (`stream_peak`);
+  stream_peak     pkv_stream_read over 8 GiB, with and without the
+                  non-temporal hint: the practical HBM read ceiling;
+  cpu_baseline    the fp64 oracle timed on the host on a bounded sample of the
+                  same workload (about --cpu-seconds of work);
+  warm            the same K steps back to back without flushing (wall clock);
+  s1_placement    the paged batches with contiguous blocks vs randomly
+                  permuted blocks (the pages' paged-vs-contiguous comparison);
+  gqa4_decode     the 64-sequence GQA-4 batch, cold;
+  prefill         the 16-sequence varlen prefill batch: algorithmic TFLOP/s
+                  against the 2.5 PFLOP/s dense bf16 MFMA peak, cold, with
+                  its own oracle baseline;
+  paged_prefill   the same batch as a paged step: cache write of the new rows,
+                  then varlen attention through the block table;
+  mixed_step      the continuous-batching step: 512 decode sequences with the
+                  in-place append, then 8 x 1024 prefill tokens, on one stream.
 Only one GPU is supported: --gpus above 1 exits with a message.
 """
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -40,6 +51,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-decode KV read GB/s (% of HBM peak) + queries/s; prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FLUSH_BYTES = 1 << 30
+COLD = ("HIP events around each step on the launch stream; the last-level cache flushed "
+        "(1 GiB overwritten) before each step, outside the timed interval")
 
 
 def log(*a):
@@ -55,7 +69,7 @@ def kv_bytes(case):
 
 # the per-partition kernel each decode workload runs: the persistent kernel,
 # or the direct grid for few units (up to two grid slots per resident wave)
-DECODE_KERNEL = {"decode_b64_gqa4": "decode_direct_kernel", "tiny_decode_fp32": "decode_direct_kernel"}
+DECODE_KERNEL = {"tiny_decode_fp32": "decode_direct_kernel"}
 
 
 def varlen_flops(case):
@@ -85,9 +99,25 @@ def traffic_for(kernel_file, workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_decode(pkv, torch, case, steps, warmup, with_events=True):
-    """Runs warmup + timed decode steps; returns wall ms/step and the mean
-    event-timed durations (ms) of the per-partition and merge kernels."""
+class Flusher:
+    """Overwrites a buffer larger than the last-level cache (outside any timed
+    interval) so that the next timed call starts cold."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
+
+
+def time_decode(pkv, torch, case, steps, warmup, flush=None):
+    """Warmup, then `steps` timed decode steps (plan + per-partition kernel +
+    merge).  With `flush`, the cache is flushed before each step and each step
+    is timed alone by events; without, the steps run back to back and the
+    wall clock is taken too.  Returns dict(step_ms, part_ms, merge_ms,
+    wall_ms)."""
     out = torch.empty_like(case.q)
     B, _, Hq, D = case.q.shape
     NB, bs, Hkv, _ = case.k_cache.shape
@@ -110,50 +140,36 @@ def time_decode(pkv, torch, case, steps, warmup, with_events=True):
             ev[2].record()
 
     for _ in range(warmup):
+        if flush is not None:
+            flush()
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i] if with_events else None)
+        if flush is not None:
+            flush()
+        step(evs[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    part = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    merge = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    return wall_ms, part, merge, out
-
-
-def time_varlen(pkv, torch, case, steps, warmup):
-    out = torch.empty_like(case.q)
-    args = (case.q, case.k, case.v, case.cu_seq_lens_q, case.cu_seq_lens_k, case.max_length_q,
-            case.max_length_k)
-    for _ in range(warmup):
-        pkv.varlen(*args, softmax_scale=case.softmax_scale, out=out)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        evs[i][0].record()
-        pkv.varlen(*args, softmax_scale=case.softmax_scale, out=out)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    return wall_ms, kern
+    return {"step_ms": sum(e[0].elapsed_time(e[2]) for e in evs) / steps,
+            "part_ms": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
+            "merge_ms": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
+            "wall_ms": None if flush is not None else wall_ms, "out": out}
 
 
 def time_call(torch, fn, steps, warmup, flush=None):
-    """Mean HIP-event time (ms) of fn() on the current stream.  With `flush`
-    (a byte tensor larger than the 256 MB last-level cache) it is
-    overwritten before every timed call, outside the timed interval, so that
-    fn() starts from a cold cache."""
+    """Mean HIP-event time (ms) of fn() on the current stream, the cache
+    flushed before every call when `flush` is given."""
     for _ in range(warmup):
+        if flush is not None:
+            flush()
         fn()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush()
         evs[i][0].record()
         fn()
         evs[i][1].record()
@@ -161,48 +177,27 @@ def time_call(torch, fn, steps, warmup, flush=None):
     return sum(e[0].elapsed_time(e[1]) for e in evs) / steps
 
 
-def paged_prefill_leg(pkv, torch, workloads, steps, warmup, dev):
-    """The prefill batch as a paged step: the new rows are written into their
-    cache slots (pkv_cache_write), then the queries attend prefix + new keys
-    straight from the paged pool (pkv_varlen_paged)."""
-    c = dict(workloads.CONFIGS["varlen_prefill"])
-    c.pop("kind")
-    pc = workloads.make_paged_prefill(device=dev, **c)
-    total, Hkv, D = pc.k_new.shape[1:]
-    row_bytes = Hkv * D * pc.k_new.element_size()
-    write_bytes = 4 * total * row_bytes         # K and V rows, read once and written once
-    fl = int(sum(4 * D * pc.q.shape[2] * int(a) * int(b)
-                 for a, b in zip(pc.q_lengths, pc.q_lengths + pc.prefix)))
-    out = torch.empty_like(pc.q)
+def varlen_call(pkv, case, out):
+    return lambda: pkv.varlen(case.q, case.k, case.v, case.cu_seq_lens_q, case.cu_seq_lens_k,
+                              case.max_length_q, case.max_length_k,
+                              softmax_scale=case.softmax_scale, out=out)
 
-    def write():
-        pkv.cache_write(pc.k_new, pc.v_new, pc.cu_seq_lens_q, pc.start, pc.k_cache, pc.v_cache,
-                        pc.block_table)
 
-    def attend():
-        pkv.varlen_paged(pc.q, pc.k_cache, pc.v_cache, pc.block_table, pc.cu_seq_lens_q,
-                         pc.seqlens_k, pc.max_length_q, pc.max_length_k,
-                         softmax_scale=pc.softmax_scale, out=out)
-
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    # reference: a plain device copy of the same rows (torch), same flush
-    kd, vd = torch.empty_like(pc.k_new), torch.empty_like(pc.v_new)
-    ck = time_call(torch, lambda: (kd.copy_(pc.k_new), vd.copy_(pc.v_new)), steps, warmup, flush)
-    del kd, vd
-    wk = time_call(torch, write, steps, warmup, flush)
-    ak = time_call(torch, attend, steps, warmup, flush)
-    sk = time_call(torch, lambda: (write(), attend()), steps, warmup, flush)
-    del flush
-    return {"workload": "paged_prefill (varlen_prefill lengths, 16-token blocks, permuted pool)",
-            "cache_write_ms": round(wk, 4), "cache_write_bytes": write_bytes,
-            "cache_write_gbs": round(write_bytes / (wk * 1e-3) / 1e9, 1),
-            "cache_write_frac_of_hbm_peak": round(write_bytes / (wk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "same_bytes_torch_copy_ms": round(ck, 4),
-            "same_bytes_torch_copy_gbs": round(write_bytes / (ck * 1e-3) / 1e9, 1),
-            "varlen_paged_ms": round(ak, 4), "flops": fl,
-            "varlen_paged_tflops": round(fl / (ak * 1e-3) / 1e12, 2),
-            "varlen_paged_frac_of_mfma_peak": round(fl / (ak * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "step_ms": round(sk, 4), "timing": "HIP events, last-level cache flushed before each call"}
+def stream_peak(pkv, torch, dev, steps=5):
+    """pkv_stream_read over 8 GiB (32x the last-level cache), with and
+    without the non-temporal hint: GB/s of the mean call."""
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wgs = 4096
+    sink = torch.empty(wgs * 4096, dtype=torch.uint8, device=dev)
+    res = {"bytes": nbytes, "workgroups": wgs}
+    for name, nt in (("nontemporal", True), ("default", False)):
+        ms = time_call(torch, lambda: pkv.stream_read(buf, sink, wgs, nt), steps, 2)
+        res[f"{name}_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    res["frac_of_spec"] = round(res["nontemporal_gbs"] / HBM_PEAK_GBS, 4)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(torch, case, seconds):
@@ -247,17 +242,177 @@ def cpu_baseline(torch, case, seconds):
                       "OpenMP over (sequence, head)"}
 
 
+def cpu_baseline_varlen(case, seconds):
+    """The fp64 varlen oracle on the host over seeded batches of 16 random
+    query rows (all heads) of the prefill batch, until about `seconds`."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    h = workloads.to_host_bits
+    q, k, v = h(case.q), h(case.k), h(case.v)
+    cq, ck = case.cu_seq_lens_q.cpu().numpy(), case.cu_seq_lens_k.cpu().numpy()
+    row_req = np.searchsorted(cq, np.arange(q.shape[1]), side="right") - 1
+    _, _, Hq, D = case.q.shape
+    rng = np.random.default_rng(54321)
+    spent, flops, nrows = 0.0, 0, 0
+    while spent < seconds:
+        rows = np.sort(rng.choice(q.shape[1], 16, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.varlen(q, k, v, cq, ck, case.max_length_q, case.max_length_k,
+                      scale=case.softmax_scale, rows=rows)
+        spent += time.perf_counter() - t0
+        lk = (ck[row_req[rows] + 1] - ck[row_req[rows]]).astype(np.int64)
+        flops += int((4 * D * Hq * lk).sum())
+        nrows += len(rows)
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"{nrows} seeded-random query rows (all {Hq} q heads, each against all its "
+                      "request's keys) of the same batch, fp64 C oracle, OpenMP over (row, head)"}
+
+
+def decode_result(args_workload, case, t, K, W, pkv, torch):
+    B, _, Hq, D = case.q.shape
+    NB, bs, Hkv, _ = case.k_cache.shape
+    kvb = kv_bytes(case)
+    gbs = kvb / (t["step_ms"] * 1e-3) / 1e9
+    ach = kvb / (t["part_ms"] * 1e-3) / 1e9
+    eff_pt = pkv.decode_partition_tokens(B, Hq, Hkv, D, bs, case.block_table.shape[1],
+                                         case.partition_tokens)
+    dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[case.q.dtype]
+    return {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(t["step_ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args_workload, "batch": B, "num_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": bs, "partition_tokens": eff_pt,
+                   "append": case.k_new is not None, "placement": getattr(case, "placement", None),
+                   "cached_tokens": int(case.lengths.sum()), "kv_bytes_per_step": kvb},
+        "timing": COLD,
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "queries_per_s": round(B / (t["step_ms"] * 1e-3), 1),
+        "kernels_ms": {"plan_and_partial": round(t["part_ms"], 4),
+                       "merge": round(t["merge_ms"], 4)},
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL.get(args_workload, "decode_partial_kernel"),
+                     "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("decode.hip", args_workload)},
+    }
+
+
+def s1_leg(pkv, torch, workloads, name, base_case, steps, warmup, flush, dev):
+    """The same decode batch with its blocks handed out in order (contiguous)
+    against the randomly permuted placement; ratio > 1 means the permuted
+    (paged) placement is slower."""
+    contig = workloads.make_config(name, device=dev, placement="contiguous")
+    tc = time_decode(pkv, torch, contig, steps, warmup, flush)
+    del contig
+    torch.cuda.empty_cache()
+    tp = time_decode(pkv, torch, base_case, steps, warmup, flush)
+    return {"permuted_ms": round(tp["step_ms"], 4), "contiguous_ms": round(tc["step_ms"], 4),
+            "ratio_permuted_over_contiguous": round(tp["step_ms"] / tc["step_ms"], 4)}
+
+
+def prefill_leg(pkv, torch, workloads, steps, warmup, flush, dev, cpu_seconds):
+    case = workloads.make_config("varlen_prefill", device=dev)
+    out = torch.empty_like(case.q)
+    fl = varlen_flops(case)
+    ms = time_call(torch, varlen_call(pkv, case, out), steps, max(warmup, 10), flush)
+    res = {"workload": "varlen_prefill", "flops_per_step": fl, "ms_per_step": round(ms, 4),
+           "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+           "frac_of_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "timing": COLD}
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_varlen(case, cpu_seconds)
+    return res
+
+
+def paged_prefill_leg(pkv, torch, workloads, steps, warmup, flush, dev):
+    """The prefill batch as a paged step: the new rows are written into their
+    cache slots (pkv_cache_write), then the queries attend prefix + new keys
+    straight from the paged pool (pkv_varlen_paged)."""
+    c = dict(workloads.CONFIGS["varlen_prefill"])
+    c.pop("kind")
+    pc = workloads.make_paged_prefill(device=dev, **c)
+    total, Hkv, D = pc.k_new.shape[1:]
+    row_bytes = Hkv * D * pc.k_new.element_size()
+    write_bytes = 4 * total * row_bytes         # K and V rows, read once and written once
+    fl = int(sum(4 * D * pc.q.shape[2] * int(a) * int(b)
+                 for a, b in zip(pc.q_lengths, pc.q_lengths + pc.prefix)))
+    out = torch.empty_like(pc.q)
+
+    def write():
+        pkv.cache_write(pc.k_new, pc.v_new, pc.cu_seq_lens_q, pc.start, pc.k_cache, pc.v_cache,
+                        pc.block_table)
+
+    def attend():
+        pkv.varlen_paged(pc.q, pc.k_cache, pc.v_cache, pc.block_table, pc.cu_seq_lens_q,
+                         pc.seqlens_k, pc.max_length_q, pc.max_length_k,
+                         softmax_scale=pc.softmax_scale, out=out)
+
+    # reference: a plain device copy of the same rows (torch), same flush
+    kd, vd = torch.empty_like(pc.k_new), torch.empty_like(pc.v_new)
+    ck = time_call(torch, lambda: (kd.copy_(pc.k_new), vd.copy_(pc.v_new)), steps, warmup, flush)
+    del kd, vd
+    wk = time_call(torch, write, steps, warmup, flush)
+    ak = time_call(torch, attend, steps, max(warmup, 10), flush)
+    sk = time_call(torch, lambda: (write(), attend()), steps, warmup, flush)
+    return {"workload": "paged_prefill (varlen_prefill lengths, 16-token blocks, permuted pool)",
+            "cache_write_ms": round(wk, 4), "cache_write_bytes": write_bytes,
+            "cache_write_gbs": round(write_bytes / (wk * 1e-3) / 1e9, 1),
+            "cache_write_frac_of_hbm_peak": round(write_bytes / (wk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "same_bytes_torch_copy_ms": round(ck, 4),
+            "same_bytes_torch_copy_gbs": round(write_bytes / (ck * 1e-3) / 1e9, 1),
+            "varlen_paged_ms": round(ak, 4), "flops": fl,
+            "varlen_paged_tflops": round(fl / (ak * 1e-3) / 1e12, 2),
+            "varlen_paged_frac_of_mfma_peak": round(fl / (ak * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "step_ms": round(sk, 4), "timing": COLD}
+
+
+def mixed_leg(pkv, torch, workloads, steps, warmup, flush, dev):
+    """The continuous-batching step: decode (append + attend) then the
+    prefill, back to back on one stream, cold."""
+    dcase, vcase = workloads.make_config("mixed_step", device=dev)
+    dk = kv_bytes(dcase)
+    vf = varlen_flops(vcase)
+    td = time_decode(pkv, torch, dcase, steps, warmup, flush)
+    out_v = torch.empty_like(vcase.q)
+    vk = time_call(torch, varlen_call(pkv, vcase, out_v), steps, max(warmup, 10), flush)
+    out_d = torch.empty_like(dcase.q)
+
+    def whole():
+        pkv.decode(dcase.q, dcase.k_cache, dcase.v_cache, dcase.block_table, dcase.cache_seqlens,
+                   dcase.k_new, dcase.v_new, softmax_scale=dcase.softmax_scale,
+                   partition_tokens=dcase.partition_tokens, out=out_d)
+        varlen_call(pkv, vcase, out_v)()
+
+    step_ms = time_call(torch, whole, steps, warmup, flush)
+    ideal_ms = dk / (HBM_PEAK_GBS * 1e9) * 1e3 + vf / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    return {"workload": "mixed_step", "ms_per_step": round(step_ms, 4),
+            "decode_kv_bytes": dk, "decode_ms": round(td["step_ms"], 4),
+            "decode_gbs": round(dk / (td["step_ms"] * 1e-3) / 1e9, 2),
+            "decode_partial_frac_of_hbm_peak": round(dk / (td["part_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_queries_per_s": round(dcase.q.shape[0] / (td["step_ms"] * 1e-3), 1),
+            "prefill_flops": vf, "prefill_ms": round(vk, 4),
+            "prefill_tflops": round(vf / (vk * 1e-3) / 1e12, 2),
+            "roofline_ms": round(ideal_ms, 4),
+            "frac_of_summed_roofline": round(ideal_ms / step_ms, 4), "timing": COLD}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b256_long",
                     choices=["decode_b256_long", "decode_b64_gqa4", "tiny_decode_fp32", "mixed_step",
-                             "varlen_prefill", "paged_prefill", "copy_1gib"])
+                             "varlen_prefill", "paged_prefill", "copy_1gib", "stream_read"])
+    ap.add_argument("--placement", default="permuted", choices=["permuted", "contiguous"],
+                    help="block placement of a decode workload (contiguous: same draws, blocks in order)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and mixed-step legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip every leg after the headline")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -285,61 +440,51 @@ def main():
                           "bytes_written_per_launch": 1 << 30}))
         return
 
+    if args.workload == "stream_read":
+        print(json.dumps({"workload": "stream_read", **stream_peak(pkv, torch, dev, K)}))
+        return
+
+    flush = Flusher(torch, dev)
+
     if args.workload == "varlen_prefill":
-        case = workloads.make_config("varlen_prefill", device=dev)
-        wall, kern = time_varlen(pkv, torch, case, K, W)
-        fl = varlen_flops(case)
-        tf = fl / (wall * 1e-3) / 1e12
-        ach = fl / (kern * 1e-3) / 1e12
+        r = prefill_leg(pkv, torch, workloads, K, W, flush, dev,
+                        0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0))
         print(json.dumps({
-            "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-            "warmup": W, "ms_per_step": round(wall, 4), "higher_is_better": True,
+            "metric": METRIC, "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+            "warmup": max(W, 10), "ms_per_step": r["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "varlen_prefill", "batch": 16, "num_heads": 32,
-                       "num_kv_heads": 8, "head_dim": 128, "flops_per_step": fl},
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": None}}))
+                       "num_kv_heads": 8, "head_dim": 128, "flops_per_step": r["flops_per_step"]},
+            "timing": COLD,
+            "roofline": {"bound": "mfma", "kernel": "varlen_persistent_kernel",
+                         "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None},
+            "cpu_baseline": r.get("cpu_baseline")}))
         return
 
     if args.workload == "paged_prefill":
-        r = paged_prefill_leg(pkv, torch, workloads, K, W, dev)
-        print(json.dumps(r))
+        print(json.dumps(paged_prefill_leg(pkv, torch, workloads, K, W, flush, dev)))
         return
 
-    log("generating", args.workload)
+    log("generating", args.workload, args.placement)
     if args.workload == "mixed_step":
-        case = workloads.make_config("mixed_step", device=dev, part="decode")
+        case = workloads.make_config("mixed_step", device=dev, part="decode",
+                                     placement=args.placement)
     else:
-        case = workloads.make_config(args.workload, device=dev)
+        case = workloads.make_config(args.workload, device=dev, placement=args.placement)
+    case.placement = args.placement
     torch.cuda.synchronize()
-    B, _, Hq, D = case.q.shape
-    NB, bs, Hkv, _ = case.k_cache.shape
+    log(f"timing {K} cold steps after {W} warmup; KV bytes/step {kv_bytes(case) / 1e9:.3f} GB")
+    t = time_decode(pkv, torch, case, K, W, flush)
+    res = decode_result(args.workload, case, t, K, W, pkv, torch)
+    log(f"decode {res['value']:.1f} GB/s cold, partial kernel {res['roofline']['achieved']:.1f} GB/s "
+        f"({t['part_ms']:.3f} ms)")
+    warm = time_decode(pkv, torch, case, K, W, None)
     kvb = kv_bytes(case)
-    log(f"timing {K} steps after {W} warmup; KV bytes/step {kvb / 1e9:.3f} GB")
-    wall, part_ms, merge_ms, _ = time_decode(pkv, torch, case, K, W)
-    gbs = kvb / (wall * 1e-3) / 1e9
-    ach = kvb / (part_ms * 1e-3) / 1e9
-    eff_pt = pkv.decode_partition_tokens(B, Hq, Hkv, D, bs, case.block_table.shape[1],
-                                         case.partition_tokens)
-    res = {
-        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": round(wall, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": str(case.q.dtype).replace("torch.", "").replace("bfloat16", "bf16").replace("float32", "f32"),
-        "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "num_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": bs, "partition_tokens": eff_pt,
-                   "append": case.k_new is not None,
-                   "cached_tokens": int(case.lengths.sum()), "kv_bytes_per_step": kvb},
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "queries_per_s": round(B / (wall * 1e-3), 1),
-        "kernels_ms": {"decode_partial": round(part_ms, 4), "decode_merge": round(merge_ms, 4)},
-        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL.get(args.workload, "decode_partial_kernel"),
-                     "achieved": round(ach, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for("decode.hip", args.workload)},
-    }
-    log(f"decode {gbs:.1f} GB/s wall, partial kernel {ach:.1f} GB/s ({part_ms:.3f} ms), merge {merge_ms:.3f} ms")
+    res["warm"] = {"ms_per_step": round(warm["wall_ms"], 4),
+                   "gbs": round(kvb / (warm["wall_ms"] * 1e-3) / 1e9, 2),
+                   "partial_kernel_ms": round(warm["part_ms"], 4),
+                   "timing": "the same steps back to back, wall clock, no flush"}
 
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
@@ -348,53 +493,48 @@ def main():
     else:
         res["cpu_baseline"] = None
 
-    if not args.no_extra and args.workload == "decode_b256_long":
+    if not args.no_extra and args.workload == "decode_b256_long" and args.placement == "permuted":
+        n, w = max(K // 2, 5), max(W // 2, 2)
+        log("stream-read ceiling")
+        res["stream_peak"] = stream_peak(pkv, torch, dev)
+        res["roofline"]["frac_of_measured_stream"] = round(
+            res["roofline"]["achieved"] / res["stream_peak"]["nontemporal_gbs"], 4)
+        log("stream", res["stream_peak"])
+        log("S1 placement: long-context batch")
+        s1 = {"decode_b256_long": s1_leg(pkv, torch, workloads, "decode_b256_long", case, n, w,
+                                         flush, dev)}
         del case
         torch.cuda.empty_cache()
+        log("GQA-4 batch")
+        g4 = workloads.make_config("decode_b64_gqa4", device=dev)
+        tg = time_decode(pkv, torch, g4, K, W, flush)
+        g4b = kv_bytes(g4)
+        res["gqa4_decode"] = {"workload": "decode_b64_gqa4", "ms_per_step": round(tg["step_ms"], 4),
+                              "gbs": round(g4b / (tg["step_ms"] * 1e-3) / 1e9, 2),
+                              "hbm_frac": round(g4b / (tg["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "kernel": DECODE_KERNEL.get("decode_b64_gqa4", "decode_partial_kernel"),
+                              "kernel_ms": round(tg["part_ms"], 4),
+                              "kernel_frac_of_hbm_peak": round(g4b / (tg["part_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "timing": COLD}
+        log("gqa4", res["gqa4_decode"])
+        s1["decode_b64_gqa4"] = s1_leg(pkv, torch, workloads, "decode_b64_gqa4", g4, n, w, flush, dev)
+        del g4
+        torch.cuda.empty_cache()
+        s1["context"] = ("the pages quote a paged kernel ~20-26% slower than a contiguous one "
+                         "(attributed to the original paper, hardware not stated)")
+        res["s1_placement"] = s1
+        log("s1", s1)
         log("prefill leg: varlen_prefill")
-        pcase = workloads.make_config("varlen_prefill", device=dev)
-        pw, pk = time_varlen(pkv, torch, pcase, max(K // 2, 5), max(W // 2, 2))
-        fl = varlen_flops(pcase)
-        res["prefill"] = {"workload": "varlen_prefill", "flops_per_step": fl,
-                          "ms_per_step": round(pw, 4), "tflops": round(fl / (pw * 1e-3) / 1e12, 2),
-                          "kernel_tflops": round(fl / (pk * 1e-3) / 1e12, 2),
-                          "frac_of_mfma_peak": round(fl / (pk * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        res["prefill"] = prefill_leg(pkv, torch, workloads, n, w, flush, dev,
+                                     0 if args.no_cpu_baseline else 5.0)
         log("prefill", res["prefill"])
-        del pcase
         torch.cuda.empty_cache()
         log("paged prefill leg")
-        res["paged_prefill"] = paged_prefill_leg(pkv, torch, workloads, max(K // 2, 5),
-                                                 max(W // 2, 2), dev)
+        res["paged_prefill"] = paged_prefill_leg(pkv, torch, workloads, n, w, flush, dev)
         log("paged prefill", res["paged_prefill"])
         torch.cuda.empty_cache()
         log("mixed step leg: mixed_step")
-        dcase, vcase = workloads.make_config("mixed_step", device=dev)
-        dk = kv_bytes(dcase)
-        vf = varlen_flops(vcase)
-        n = max(K // 2, 5)
-        dw, dpart, dmerge, _ = time_decode(pkv, torch, dcase, n, max(W // 2, 2))
-        vw, vk = time_varlen(pkv, torch, vcase, n, max(W // 2, 2))
-        # the whole step back to back: decode (append + attend) then prefill
-        out_d = torch.empty_like(dcase.q)
-        out_v = torch.empty_like(vcase.q)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n):
-            pkv.decode(dcase.q, dcase.k_cache, dcase.v_cache, dcase.block_table, dcase.cache_seqlens,
-                       dcase.k_new, dcase.v_new, softmax_scale=dcase.softmax_scale,
-                       partition_tokens=dcase.partition_tokens, out=out_d)
-            pkv.varlen(vcase.q, vcase.k, vcase.v, vcase.cu_seq_lens_q, vcase.cu_seq_lens_k,
-                       vcase.max_length_q, vcase.max_length_k, softmax_scale=vcase.softmax_scale,
-                       out=out_v)
-        torch.cuda.synchronize()
-        step_ms = (time.perf_counter() - t0) * 1e3 / n
-        ideal_ms = dk / (HBM_PEAK_GBS * 1e9) * 1e3 + vf / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
-        res["mixed_step"] = {"workload": "mixed_step", "ms_per_step": round(step_ms, 4),
-                             "decode_kv_bytes": dk, "decode_gbs": round(dk / (dpart + dmerge) / 1e6, 2),
-                             "decode_queries_per_s": round(dcase.q.shape[0] / (dpart + dmerge) * 1e3, 1),
-                             "prefill_flops": vf, "prefill_tflops": round(vf / (vk * 1e-3) / 1e12, 2),
-                             "roofline_ms": round(ideal_ms, 4),
-                             "frac_of_summed_roofline": round(ideal_ms / step_ms, 4)}
+        res["mixed_step"] = mixed_leg(pkv, torch, workloads, n, w, flush, dev)
         log("mixed", res["mixed_step"])
     print(json.dumps(res), flush=True)
 

@@ -412,6 +412,20 @@ int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
                     const int32_t* dst, int n, int num_blocks, int block_size, int num_kv_heads,
                     int head_dim, int32_t* err_flag, void* stream);
 
+/* ------------------------------------------------------ measurement aid
+ *
+ * Reads `bytes` bytes of the device buffer `buf` once, as a plain stream
+ * (16-byte loads, grid-stride, `workgroups` workgroups of 256 lanes), with
+ * the non-temporal cache hint the decode kernels put on their K/V loads
+ * (nontemporal = 1) or none (0).  It computes nothing; timing it gives the
+ * practical HBM read ceiling the decode bandwidth is compared with.  `sink`
+ * is device memory of workgroups * 4096 bytes that the kernel may write (in
+ * practice it writes nothing).  bytes must be a multiple of 16; workgroups in
+ * 1 .. 65535.  PKV_EINVAL on bad arguments.
+ */
+int pkv_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, int nontemporal,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ __all__ = [
     "check_varlen_args", "check_cache_write_args", "check_varlen_paged_args", "status_string",
     "abi_version", "lib_path", "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
     "BlockManager", "OutOfBlocks", "copy_blocks", "decode_noalloc",
-    "DECODE_NOALLOC_SCRATCH_BYTES",
+    "DECODE_NOALLOC_SCRATCH_BYTES", "stream_read",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENOMEM = 0, 1, 2, 3, 4, 5
@@ -102,6 +102,8 @@ def _load():
         L.pkv_bm_table.restype = I
         L.pkv_copy_blocks.argtypes = [I, P, P, P, P, I, I, I, I, I, P, P]
         L.pkv_copy_blocks.restype = I
+        L.pkv_stream_read.argtypes = [P, SZ, P, I, I, P]
+        L.pkv_stream_read.restype = I
         _lib = L
     return _lib
 
@@ -524,3 +526,18 @@ def copy_blocks(k_cache, v_cache, src, dst, *, err_flag=None, stream=None):
                              _stream(stream))
     if rc:
         raise PkvError(rc, "pkv_copy_blocks")
+
+
+def stream_read(buf, sink, workgroups=4096, nontemporal=True, stream=None):
+    """Measurement aid: one plain streaming read of the device tensor `buf`
+    (pkv_stream_read).  `sink` is a device tensor of at least workgroups *
+    4096 bytes."""
+    lib = _load()
+    _need_gpu(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < workgroups * 4096 or not buf.is_contiguous():
+        raise ValueError("sink too small or buf not contiguous")
+    rc = lib.pkv_stream_read(_ptr(buf), nbytes, _ptr(sink), int(workgroups), int(bool(nontemporal)),
+                             _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_stream_read")

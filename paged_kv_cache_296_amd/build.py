@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["pkv_api.hip", "decode.hip", "varlen.hip", "cache_write.hip", "block_manager.cpp"]
+SOURCES = ["pkv_api.hip", "decode.hip", "varlen.hip", "cache_write.hip", "block_manager.cpp",
+           "stream_read.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

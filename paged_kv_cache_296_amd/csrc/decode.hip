@@ -106,15 +106,15 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
 }
 
 // Cache policy of the K/V tile loads (the buffer instructions' aux bits:
-// 1 = sc0, 2 = nt, 16 = sc1).  The persistent kernel streams each K/V byte
-// once per call through a working set far above the 256 MB last-level
-// cache, and the non-temporal hint measured 4 % faster there (long-context
-// batch 5.93 -> 6.16 TB/s, the mixed step's decode half 5.96 -> 6.39).  The
-// direct grid serves small batches whose K/V partly stays cached from one
-// decode step to the next; the hint costs it 6 % (64 sequences, 4.91 -> 4.58
-// TB/s), sc1 13 %, so it keeps the default policy.
+// 1 = sc0, 2 = nt, 16 = sc1).  Each K/V byte is read once per call, and
+// with the last-level cache flushed before every step the non-temporal hint
+// is the faster policy for both launch forms: the persistent kernel on the
+// long-context batch 5.93 -> 6.16 TB/s (the mixed step's decode half 5.96 ->
+// 6.39); the direct grid on 1 / 2 / 4 long GQA-4 sequences 54.5 -> 41.1,
+// 71.5 -> 49.2, 116 -> 73 us.  (Without the flush, repeated steps over a
+// small batch find part of it cached, and the hint then cost the direct
+// grid 6 % at 64 sequences, a batch the persistent kernel serves now.)
 constexpr int kCpolStream = 2;
-constexpr int kCpolDefault = 0;
 constexpr int kRsrcFlags = 0x00020000;  // gfx9-family buffer descriptor word 3
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* base, int bytes) {
@@ -630,7 +630,7 @@ void decode_direct_kernel(DecodeArgs a) {
   const int Lp = L + a.has_new;
   const bool bad = L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS;
   if (part > 0 && (bad || part * a.part_tokens >= Lp)) return;
-  decode_unit<BF16, D, BS, kCpolDefault>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh, hc);
+  decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh, hc);
 }
 
 // Work list for the persistent kernel, one workgroup.  Every sequence's

@@ -18,13 +18,16 @@ bool decode_shape_ok(int head_dim, int block_size) {
   return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
 }
 
-// Library choice of partition length: 512 tokens -- on GQA-4 batches of 32 to
-// 256 sequences it was the best or within 5 % of the best length, while the
-// 1024-token length was the worst at every batch size and longer ones leave
-// SIMDs idle at small batches -- halved (down to 128 tokens) while the
-// expected units, sequences averaging half their table span, would not give
-// each of the 1024 SIMDs one; the whole row when it is shorter.  Always a
-// block multiple within the LDS slice.
+// Library choice of partition length: 512 tokens, halved (down to 128) while
+// the expected units -- sequences averaging half their table span -- would
+// not give each of the 2048 resident waves of the per-partition kernel two
+// of them; the whole row when it is shorter.  Always a block multiple within
+// the LDS slice.  Measured with the last-level cache flushed before each
+// step, GQA-4 batches of 512..4096 tokens at 32 / 64 / 128 / 256 sequences:
+// 128-token partitions 92 / 165 / 272 / 472 us, 256: 127 / 149 / 272 / 466,
+// 512: 122 / 202 / 253 / 491, 1024: 123 / 204 / 346 / 459; this rule picks
+// 128 / 256 / 512 / 512 (the previous target of one unit per SIMD picked 512
+// for 64 sequences).
 int choose_partition(int batch, int num_kv_heads, int head_chunks, int block_size,
                      int max_blocks_per_seq) {
   const long long span = (long long)max_blocks_per_seq * block_size;
@@ -32,7 +35,7 @@ int choose_partition(int batch, int num_kv_heads, int head_chunks, int block_siz
   const long long base_units = (long long)batch * num_kv_heads * head_chunks;
   const long long floor_p = block_size > 128 ? block_size : 128;
   long long p = 512;
-  while (p / 2 >= floor_p && base_units * ((span / 2 + p - 1) / p) < 1024) p /= 2;
+  while (p / 2 >= floor_p && base_units * ((span / 2 + p - 1) / p) < 4096) p /= 2;
   if (p > cap) p = cap;
   p -= p % block_size;
   if (p < block_size) p = block_size;

@@ -286,11 +286,14 @@ def make_paged_prefill(*, seed, dtype, batch, num_heads, num_kv_heads, head_dim,
                             softmax_scale=softmax_scale, q_lengths=lq, prefix=pre, seed=seed)
 
 
-def make_config(name: str, device="cpu", part=None):
+def make_config(name: str, device="cpu", part=None, **overrides):
     """The named workload: a DecodeCase, a VarlenCase, or for the mixed step
-    (decode, varlen) -- or just one of them with part="decode"/"prefill"."""
+    (decode, varlen) -- or just one of them with part="decode"/"prefill".
+    `overrides` replace entries of a decode or varlen workload (e.g.
+    placement="contiguous": the same draws with blocks handed out in order)."""
     c = dict(CONFIGS[name])
     kind = c.pop("kind")
+    c.update(overrides)
     if kind == "decode":
         return make_decode(device=device, **c)
     if kind == "varlen":
