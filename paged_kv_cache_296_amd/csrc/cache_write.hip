@@ -7,14 +7,15 @@
 // sequence b and is copied, bit for bit, to slot p mod block_size of
 // physical block block_table[b][p / block_size], for K and for V.
 //
-// How: one wave per 2 consecutive packed rows.  Everything that locates a
-// row -- its request (one load of cu per lane and a ballot, or a binary
-// search for large batches), its token position, its table entry -- is
-// wave-uniform and runs on the scalar unit; the 64 lanes then move the rows'
+// How: one wave per 2 consecutive packed rows.  The 64 lanes move the rows'
 // Hkv * D elements (2 KB per row of K at 8 kv heads x 128 bf16) in 16-byte
-// pieces, issuing the loads of both rows of K and V before any store, so
-// each lane has 8 loads in flight (1, 2, 4 and 8 rows per wave measured
-// 40.2, 39.4, 40.8 and 52 us on the 16-request prefill batch).  A row is contiguous at both ends (a
+// pieces, issuing the loads of both rows of K and V first -- each lane has 8
+// loads in flight -- and only then locating the rows' slots: everything
+// that locates a row -- its request (one load of cu per lane and a ballot,
+// or a binary search for large batches), its token position, its table
+// entry -- is wave-uniform and runs on the scalar unit, three dependent
+// round trips that the loads now overlap (39.0-39.7 -> 36.2-36.4 us on the
+// 16-request prefill batch; 1 and 4 rows per wave 39.6 and 37.5 us).  A row is contiguous at both ends (a
 // token row of the cache is [Hkv][D] like a packed row), so both sides are
 // coalesced.  The packed rows are read once, with the non-temporal hint
 // (measured 28 % faster than plain loads on the 16-request prefill batch:
@@ -73,9 +74,25 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
   const long long r0 = gw * kRowsPerWave;
   if (r0 >= a.total || a.batch <= 0) return;
 
-  // locate this wave's rows (uniform: scalar registers)
+  // the rows' loads go out first: their source depends only on the row
+  // number, and the lookups below (cu, then start, then the table entry)
+  // are three dependent round trips that now overlap them
   const int n16 = a.row_bytes / 16;
   const int nrows = (int)min((long long)kRowsPerWave, a.total - r0);
+  u32x4 kx[kRowsPerWave][kMaxPieces], vx[kRowsPerWave][kMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int c = lane + 64 * j;
+      if (i < nrows && c < n16) {
+        const long long off = (r0 + i) * a.row_bytes + 16 * c;
+        kx[i][j] = load_once((const char*)a.k + off);
+        vx[i][j] = load_once((const char*)a.v + off);
+      }
+    }
+
+  // locate this wave's rows (uniform: scalar registers)
   long long src[kRowsPerWave], dst[kRowsPerWave];
   bool ok[kRowsPerWave];
   int b = __builtin_amdgcn_readfirstlane(request_of(a.cu, a.batch, (int)r0, lane));
@@ -109,18 +126,7 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
   }
   if (err && a.err_flag && lane == 0) atomicOr(a.err_flag, (int)err);
 
-  // all loads of the wave's rows first, then all stores
-  u32x4 kx[kRowsPerWave][kMaxPieces], vx[kRowsPerWave][kMaxPieces];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i)
-#pragma unroll
-    for (int j = 0; j < kMaxPieces; ++j) {
-      const int c = lane + 64 * j;
-      if (ok[i] && c < n16) {
-        kx[i][j] = load_once((const char*)a.k + src[i] + 16 * c);
-        vx[i][j] = load_once((const char*)a.v + src[i] + 16 * c);
-      }
-    }
+  // then the stores of the rows that have a slot
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i)
 #pragma unroll
