@@ -314,12 +314,24 @@ def s1_leg(pkv, torch, workloads, name, base_case, steps, warmup, flush, dev):
             "ratio_permuted_over_contiguous": round(tp["step_ms"] / tc["step_ms"], 4)}
 
 
-def prefill_leg(pkv, torch, workloads, steps, warmup, flush, dev, cpu_seconds):
-    case = workloads.make_config("varlen_prefill", device=dev)
+def make_prefill_case(workloads, name, dev):
+    """varlen_prefill: the 16-request batch; varlen_uniform: 16 requests of
+    2048 query rows and 4096 keys each (the kernel's steady state, for
+    counters)."""
+    if name == "varlen_uniform":
+        return workloads.make_varlen(seed=1, dtype="bf16", batch=16, num_heads=32, num_kv_heads=8,
+                                     head_dim=128, q_lengths=("fixed", 2048),
+                                     k_lengths=("fixed", 4096), device=dev)
+    return workloads.make_config(name, device=dev)
+
+
+def prefill_leg(pkv, torch, workloads, steps, warmup, flush, dev, cpu_seconds,
+                name="varlen_prefill"):
+    case = make_prefill_case(workloads, name, dev)
     out = torch.empty_like(case.q)
     fl = varlen_flops(case)
     ms = time_call(torch, varlen_call(pkv, case, out), steps, max(warmup, 10), flush)
-    res = {"workload": "varlen_prefill", "flops_per_step": fl, "ms_per_step": round(ms, 4),
+    res = {"workload": name, "flops_per_step": fl, "ms_per_step": round(ms, 4),
            "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
            "frac_of_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "timing": COLD}
@@ -407,7 +419,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b256_long",
                     choices=["decode_b256_long", "decode_b64_gqa4", "tiny_decode_fp32", "mixed_step",
-                             "varlen_prefill", "paged_prefill", "copy_1gib", "stream_read"])
+                             "varlen_prefill", "varlen_uniform", "paged_prefill", "copy_1gib",
+                             "stream_read"])
     ap.add_argument("--placement", default="permuted", choices=["permuted", "contiguous"],
                     help="block placement of a decode workload (contiguous: same draws, blocks in order)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -446,14 +459,14 @@ def main():
 
     flush = Flusher(torch, dev)
 
-    if args.workload == "varlen_prefill":
+    if args.workload in ("varlen_prefill", "varlen_uniform"):
         r = prefill_leg(pkv, torch, workloads, K, W, flush, dev,
-                        0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0))
+                        0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0), args.workload)
         print(json.dumps({
             "metric": METRIC, "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
             "warmup": max(W, 10), "ms_per_step": r["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "varlen_prefill", "batch": 16, "num_heads": 32,
+            "config": {"workload": args.workload, "batch": 16, "num_heads": 32,
                        "num_kv_heads": 8, "head_dim": 128, "flops_per_step": r["flops_per_step"]},
             "timing": COLD,
             "roofline": {"bound": "mfma", "kernel": "varlen_persistent_kernel",
