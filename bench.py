@@ -23,6 +23,9 @@ The same JSON line carries
                   ceiling (`stream_peak`);
   stream_peak     pkv_stream_read over 8 GiB, with and without the
                   non-temporal hint: the practical HBM read ceiling;
+  mfma_peak       pkv_mfma_peak, a register-only loop of the bf16 matrix-core
+                  product the prefill tiles use: the practical MFMA ceiling
+                  at the clock the part holds under that load;
   cpu_baseline    the fp64 oracle timed on the host on a bounded sample of the
                   same workload (about --cpu-seconds of work);
   warm            the same K steps back to back without flushing (wall clock);
@@ -197,6 +200,31 @@ def stream_peak(pkv, torch, dev, steps=5):
     res["frac_of_spec"] = round(res["nontemporal_gbs"] / HBM_PEAK_GBS, 4)
     del buf, sink
     torch.cuda.empty_cache()
+    return res
+
+
+def mfma_peak(pkv, torch, dev, steps=5):
+    """pkv_mfma_peak: a register-only loop of the bf16 32x32x16 matrix-core
+    product the prefill tiles use, 2 and 4 workgroups (2 and 4 waves per
+    SIMD) per compute unit, about 2 ms per call: TFLOP/s of the mean call,
+    the better of the two."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {"instruction": "v_mfma_f32_32x32x16_bf16", "compute_units": cus}
+    best = 0.0
+    for per_cu in (2, 4):
+        wgs = per_cu * cus
+        iters = 32768 // per_cu
+        sink = torch.empty(wgs * 1024, dtype=torch.uint8, device=dev)
+        fl = [0]
+
+        def run():
+            fl[0] = pkv.mfma_peak(sink, wgs, iters)
+        ms = time_call(torch, run, steps, 3)
+        tf = fl[0] / (ms * 1e-3) / 1e12
+        res[f"tflops_{per_cu}_per_cu"] = round(tf, 1)
+        best = max(best, tf)
+    res["tflops"] = round(best, 1)
+    res["frac_of_spec"] = round(best / MFMA_BF16_PEAK_TFLOPS, 4)
     return res
 
 
@@ -420,7 +448,7 @@ def main():
     ap.add_argument("--workload", default="decode_b256_long",
                     choices=["decode_b256_long", "decode_b64_gqa4", "tiny_decode_fp32", "mixed_step",
                              "varlen_prefill", "varlen_uniform", "paged_prefill", "copy_1gib",
-                             "stream_read"])
+                             "stream_read", "mfma_peak"])
     ap.add_argument("--placement", default="permuted", choices=["permuted", "contiguous"],
                     help="block placement of a decode workload (contiguous: same draws, blocks in order)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -457,11 +485,16 @@ def main():
         print(json.dumps({"workload": "stream_read", **stream_peak(pkv, torch, dev, K)}))
         return
 
+    if args.workload == "mfma_peak":
+        print(json.dumps({"workload": "mfma_peak", **mfma_peak(pkv, torch, dev, K)}))
+        return
+
     flush = Flusher(torch, dev)
 
     if args.workload in ("varlen_prefill", "varlen_uniform"):
         r = prefill_leg(pkv, torch, workloads, K, W, flush, dev,
                         0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0), args.workload)
+        mp = mfma_peak(pkv, torch, dev)
         print(json.dumps({
             "metric": METRIC, "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
             "warmup": max(W, 10), "ms_per_step": r["ms_per_step"], "higher_is_better": True,
@@ -471,7 +504,9 @@ def main():
             "timing": COLD,
             "roofline": {"bound": "mfma", "kernel": "varlen_persistent_kernel",
                          "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None},
+                         "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None,
+                         "frac_of_measured_mfma": round(r["tflops"] / mp["tflops"], 4)},
+            "mfma_peak": mp,
             "cpu_baseline": r.get("cpu_baseline")}))
         return
 
@@ -537,13 +572,20 @@ def main():
                          "(attributed to the original paper, hardware not stated)")
         res["s1_placement"] = s1
         log("s1", s1)
+        log("MFMA-loop ceiling")
+        res["mfma_peak"] = mfma_peak(pkv, torch, dev)
+        log("mfma", res["mfma_peak"])
         log("prefill leg: varlen_prefill")
         res["prefill"] = prefill_leg(pkv, torch, workloads, n, w, flush, dev,
                                      0 if args.no_cpu_baseline else 5.0)
+        res["prefill"]["frac_of_measured_mfma"] = round(
+            res["prefill"]["tflops"] / res["mfma_peak"]["tflops"], 4)
         log("prefill", res["prefill"])
         torch.cuda.empty_cache()
         log("paged prefill leg")
         res["paged_prefill"] = paged_prefill_leg(pkv, torch, workloads, n, w, flush, dev)
+        res["paged_prefill"]["varlen_paged_frac_of_measured_mfma"] = round(
+            res["paged_prefill"]["varlen_paged_tflops"] / res["mfma_peak"]["tflops"], 4)
         log("paged prefill", res["paged_prefill"])
         torch.cuda.empty_cache()
         log("mixed step leg: mixed_step")

@@ -426,6 +426,18 @@ int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
 int pkv_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, int nontemporal,
                     void* stream);
 
+/* Runs `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 products
+ * (32768 flops each) in every wave of `workgroups` workgroups of 256 lanes,
+ * with operands held in registers and no memory traffic: timing it gives the
+ * practical dense bf16 matrix-core ceiling (at the clock the part sustains
+ * under that load) that the prefill throughput is compared with.  Flops per
+ * call: workgroups * 4 waves * iters * 4 * 32768.  `sink` is device memory of
+ * workgroups * 1024 bytes that the kernel may write (in practice it writes
+ * nothing).  workgroups in 1 .. 65535, iters >= 0.  PKV_EINVAL on bad
+ * arguments.
+ */
+int pkv_mfma_peak(void* sink, int workgroups, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

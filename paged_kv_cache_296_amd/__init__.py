@@ -22,7 +22,7 @@ __all__ = [
     "check_varlen_args", "check_cache_write_args", "check_varlen_paged_args", "status_string",
     "abi_version", "lib_path", "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
     "BlockManager", "OutOfBlocks", "copy_blocks", "decode_noalloc",
-    "DECODE_NOALLOC_SCRATCH_BYTES", "stream_read",
+    "DECODE_NOALLOC_SCRATCH_BYTES", "stream_read", "mfma_peak",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENOMEM = 0, 1, 2, 3, 4, 5
@@ -104,6 +104,8 @@ def _load():
         L.pkv_copy_blocks.restype = I
         L.pkv_stream_read.argtypes = [P, SZ, P, I, I, P]
         L.pkv_stream_read.restype = I
+        L.pkv_mfma_peak.argtypes = [P, I, I, P]
+        L.pkv_mfma_peak.restype = I
         _lib = L
     return _lib
 
@@ -541,3 +543,17 @@ def stream_read(buf, sink, workgroups=4096, nontemporal=True, stream=None):
                              _stream(stream))
     if rc:
         raise PkvError(rc, "pkv_stream_read")
+
+
+def mfma_peak(sink, workgroups, iters, stream=None):
+    """Measurement aid: a register-only loop of bf16 32x32x16 matrix-core
+    products (pkv_mfma_peak); returns the flops of the call.  `sink` is a
+    device tensor of at least workgroups * 1024 bytes."""
+    lib = _load()
+    _need_gpu(sink)
+    if sink.numel() * sink.element_size() < workgroups * 1024:
+        raise ValueError("sink too small")
+    rc = lib.pkv_mfma_peak(_ptr(sink), int(workgroups), int(iters), _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_mfma_peak")
+    return int(workgroups) * 4 * int(iters) * 4 * 32768

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = ["pkv_api.hip", "decode.hip", "varlen.hip", "cache_write.hip", "block_manager.cpp",
-           "stream_read.hip"]
+           "stream_read.hip", "mfma_peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -28,11 +28,15 @@
 //    key order of each 8-key half matches the order of the S^T accumulator,
 //    so P^T is the S^T accumulator rounded to bf16, with no data movement.
 //    O^T keeps one query row per lane, so the softmax rescale is lane-local.
-//  * Online softmax in the exp2 domain with a lazy reference: the running
-//    reference max of a row only moves (and the accumulators are rescaled)
-//    when a tile's max exceeds it by more than 2^8, so exponentials stay
-//    below 256 and most tiles skip the rescale.  The final division by the
-//    row sum happens once in the epilogue; bf16 output rounds to nearest even.
+//  * Online softmax in the exp2 domain with a lazy reference: a row's
+//    exponentials are taken against its running reference before the tile's
+//    max is known, and the reference only moves (the accumulators rescaled,
+//    the tile's exponentials taken again) when the lane's sum of them shows
+//    that the tile's max has run more than 2^8 past it; so exponentials stay
+//    below 2^13 and the row max is taken only on the first and last tile of
+//    an item and on the rare tile that moves the reference.  The final
+//    division by the row sum happens once in the epilogue; bf16 output
+//    rounds to nearest even.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,6 +66,7 @@ constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kWaveRows = 32;    // query rows per wave
 constexpr int kKeys = 64;        // keys per LDS tile
 constexpr float kLazy = 8.f;     // log2 of the largest exponential kept before a rescale
+constexpr float kLazySum = 8192.f;  // 32 exponentials of at most 2^8 each
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u, kErrCu = 4u, kErrMaxLen = 8u;
 
 template <int D>
@@ -501,7 +506,6 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
     if (j + 2 < nk) issue(kg, j + 2, kbuf(j));
     issue(vg, j + 1, vbuf(j + 1));
     if (!wave_active) return;
-    const float neg_m = softmax_head<D, false>(sc, acc, m_ref, l_run, c, kKeys, hh);
     float psum = 0.f;
     u32 pw[2][8];
     // the interleaved phase runs at raised wave priority, so that the other
@@ -509,8 +513,19 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
     // (without it, or with P.V raised instead: 7 % slower at head_dim 64,
     // 2-3 % on short items at head_dim 128, the 16-request batch even)
     __builtin_amdgcn_s_setprio(1);
-    qk_and_exp<D>(kofs(j + 1), qr, koff, sn, sc, c, neg_m, psum, pw);
+    qk_and_exp<D>(kofs(j + 1), qr, koff, sn, sc, c, -m_ref, psum, pw);
     __builtin_amdgcn_s_setprio(0);
+    // the exponentials were taken against the current reference before the
+    // tile's max is known; the lane's sum of its 32 of them bounds each, so
+    // only a sum past 32 * 2^8 (or inf / NaN) asks for the max, which then
+    // lies more than 2^8 above the reference: the reference moves and the
+    // exponentials are taken again
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kLazySum)) != 0) {
+      const float neg_m = softmax_head<D, false>(sc, acc, m_ref, l_run, c, kKeys, hh);
+      psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) exp_pair(sc, e, c, neg_m, psum, pw);
+    }
     l_run += psum;
     pv<D>(vofs(j), voff, pw, acc);
   };
@@ -519,7 +534,12 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
     issue(vg, 0, vbuf(0));
     if (nk > 1) issue(kg, 1, kbuf(1));
     wait_all();
-    if (wave_active) qk_only<D>(kofs(0), qr, koff, sa);
+    if (wave_active) {
+      qk_only<D>(kofs(0), qr, koff, sa);
+      // a full first tile sets the reference (the last tile, also when it
+      // is the first, takes its own max below)
+      if (nk > 1) softmax_head<D, false>(sa, acc, m_ref, l_run, c, kKeys, hh);
+    }
     int j = 0;
     for (; j + 2 < nk; j += 2) {
       step(j, sa, sb);
