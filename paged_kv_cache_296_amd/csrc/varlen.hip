@@ -134,6 +134,18 @@ __device__ __forceinline__ void load_to_lds(u32x4 rs, int voff, u32 lds_addr) {
                : "memory", "m0");
 }
 
+// This wave's byte offset inside an LDS tile (its share of the tile's 1 KB
+// loads).  Recomputed at each use: the value is hidden from the optimiser, so
+// the tile addresses built on it are not all hoisted out of the tile loop,
+// where each would hold a scalar register of its own (and push others into
+// spill slots).
+template <int D>
+__device__ __forceinline__ u32 wave_lds_offset(int wave) {
+  u32 w = (u32)wave;
+  asm volatile("" : "+s"(w));
+  return w * (u32)(Geo<D>::NLOAD * 1024);
+}
+
 // Moves rows t0 .. t0+valid-1 (valid <= 64) of K or V into one LDS tile.
 // Lane offsets `off` address the full tile; rows past `valid` are clamped to
 // the last valid row (their scores are masked, so any finite copy will do).
@@ -142,11 +154,12 @@ __device__ __forceinline__ void issue_tile(const char* g, long long t0, int vali
                                            lds_char* tile, int wave, int lane, const int* off) {
   using G = Geo<D>;
   const u32x4 rs = vsharp(g + t0 * tok, valid * tok);
+  const u32 t = (u32)(uintptr_t)tile + wave_lds_offset<D>(wave);
 #pragma unroll
   for (int i = 0; i < G::NLOAD; ++i) {
     int o = off[i];
     if (PARTIAL) o -= max(((wave * G::NLOAD + i) * 64 + lane) / G::CH - (valid - 1), 0) * tok;
-    load_to_lds(rs, o, (u32)(uintptr_t)(tile + (wave * G::NLOAD + i) * 1024));
+    load_to_lds(rs, o, t + i * 1024);
   }
 }
 
@@ -169,12 +182,12 @@ __device__ __forceinline__ void issue_tile_paged(const char* cache, const int* s
   const int j = tf / bs;
   const int pb = __builtin_amdgcn_readfirstlane(slice[j]);
   const u32x4 rs = vsharp(cache + (long long)pb * bs * tok, bs * tok);
+  const u32 t = (u32)(uintptr_t)tile + wave_lds_offset<D>(wave);
 #pragma unroll
   for (int i = 0; i < G::NLOAD; ++i) {
     int tl = tw + i * RPI + lane / G::CH;
     if (PARTIAL) tl = min(tl, len_k - 1);
-    load_to_lds(rs, (tl - j * bs) * tok + coff[i],
-                (u32)(uintptr_t)(tile + (wave * G::NLOAD + i) * 1024));
+    load_to_lds(rs, (tl - j * bs) * tok + coff[i], t + i * 1024);
   }
 }
 
