@@ -5,10 +5,12 @@
 // the one the prefill tiles use, v_mfma_f32_32x32x16_bf16 (32 x 32 x 16, 32768
 // flops), issued in four independent accumulator chains per wave so that a
 // chain's latency never stalls the pipe; 256-thread workgroups, one wave per
-// SIMD each.  The operands are small lane-dependent values of both signs, so
-// the accumulators stay finite; they are reduced and stored only if the sum
-// hits a fixed pattern, so the products cannot be dropped and nothing is
-// written in practice.
+// SIMD each.  The operands are bf16 values with hashed signs and mantissas
+// (every bit pattern of a random matrix, so the datapath toggles as much as
+// on real data; the clock the part holds depends on it) and a fixed small
+// exponent, so the accumulators stay finite; they are reduced and stored
+// only if the sum hits a fixed pattern, so the products cannot be dropped
+// and nothing is written in practice.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,13 +26,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kChains = 4;
 
 __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* sink) {
-  const int lane = threadIdx.x & 63;
-  bf16x8 a, b;
+  // a different operand pair for each chain, so that consecutive products
+  // never see the same inputs
+  bf16x8 a[kChains], b[kChains];
+  uint32_t h = (blockIdx.x * 256u + threadIdx.x) * 0x9E3779B9u + 0x7F4A7C15u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)((float)(((lane + i) & 7) - 4) * 0.0078125f);
-    b[i] = (__bf16)((float)(((lane * 3 + i) & 7) - 3) * 0.0078125f);
-  }
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // sign and 7 mantissa bits from a xorshift stream; exponent of 2^-7
+      h ^= h << 13;
+      h ^= h >> 17;
+      h ^= h << 5;
+      a[c][i] = __builtin_bit_cast(__bf16, (unsigned short)((h & 0x807Fu) | 0x3C00u));
+      b[c][i] = __builtin_bit_cast(__bf16, (unsigned short)(((h >> 16) & 0x807Fu) | 0x3C00u));
+    }
   f32x16 acc[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c)
@@ -39,7 +49,7 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* sink) 
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
