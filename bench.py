@@ -391,10 +391,16 @@ def paged_prefill_leg(pkv, torch, workloads, steps, warmup, flush, dev):
                          pc.seqlens_k, pc.max_length_q, pc.max_length_k,
                          softmax_scale=pc.softmax_scale, out=out)
 
-    # reference: a plain device copy of the same rows (torch), same flush
+    # references: a plain device copy of the same rows (torch), and the
+    # library's plain copy kernel over the same byte count (pkv_stream_copy,
+    # one buffer holding K and V), same flush
     kd, vd = torch.empty_like(pc.k_new), torch.empty_like(pc.v_new)
     ck = time_call(torch, lambda: (kd.copy_(pc.k_new), vd.copy_(pc.v_new)), steps, warmup, flush)
     del kd, vd
+    src = torch.empty(write_bytes // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sc = time_call(torch, lambda: pkv.stream_copy(src, dst), steps, warmup, flush)
+    del src, dst
     wk = time_call(torch, write, steps, warmup, flush)
     ak = time_call(torch, attend, steps, max(warmup, 10), flush)
     sk = time_call(torch, lambda: (write(), attend()), steps, warmup, flush)
@@ -404,6 +410,9 @@ def paged_prefill_leg(pkv, torch, workloads, steps, warmup, flush, dev):
             "cache_write_frac_of_hbm_peak": round(write_bytes / (wk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "same_bytes_torch_copy_ms": round(ck, 4),
             "same_bytes_torch_copy_gbs": round(write_bytes / (ck * 1e-3) / 1e9, 1),
+            "same_bytes_stream_copy_ms": round(sc, 4),
+            "same_bytes_stream_copy_gbs": round(write_bytes / (sc * 1e-3) / 1e9, 1),
+            "cache_write_frac_of_stream_copy": round(sc / wk, 4),
             "varlen_paged_ms": round(ak, 4), "flops": fl,
             "varlen_paged_tflops": round(fl / (ak * 1e-3) / 1e12, 2),
             "varlen_paged_frac_of_mfma_peak": round(fl / (ak * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

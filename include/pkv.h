@@ -426,6 +426,15 @@ int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
 int pkv_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, int nontemporal,
                     void* stream);
 
+/* Copies `bytes` bytes (a multiple of 16, below 2 GiB) from device buffer
+ * `src` to device buffer `dst` (not overlapping) with `workgroups`
+ * workgroups of 256 lanes: 16-byte loads with the non-temporal hint, eight
+ * in flight per lane, and 16-byte stores.  Timing it gives the practical
+ * ceiling for kernels that write every byte they read, which the paged
+ * cache write is compared with.  PKV_EINVAL on bad arguments.
+ */
+int pkv_stream_copy(const void* src, void* dst, size_t bytes, int workgroups, void* stream);
+
 /* Runs `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 products
  * (32768 flops each) in every wave of `workgroups` workgroups of 256 lanes,
  * with operands held in registers and no memory traffic: timing it gives the

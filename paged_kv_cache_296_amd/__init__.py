@@ -22,7 +22,7 @@ __all__ = [
     "check_varlen_args", "check_cache_write_args", "check_varlen_paged_args", "status_string",
     "abi_version", "lib_path", "ERR_BLOCK", "ERR_SPAN", "ERR_CU", "ERR_MAXLEN",
     "BlockManager", "OutOfBlocks", "copy_blocks", "decode_noalloc",
-    "DECODE_NOALLOC_SCRATCH_BYTES", "stream_read", "mfma_peak",
+    "DECODE_NOALLOC_SCRATCH_BYTES", "stream_read", "stream_copy", "mfma_peak",
 ]
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENOMEM = 0, 1, 2, 3, 4, 5
@@ -104,6 +104,8 @@ def _load():
         L.pkv_copy_blocks.restype = I
         L.pkv_stream_read.argtypes = [P, SZ, P, I, I, P]
         L.pkv_stream_read.restype = I
+        L.pkv_stream_copy.argtypes = [P, P, SZ, I, P]
+        L.pkv_stream_copy.restype = I
         L.pkv_mfma_peak.argtypes = [P, I, I, P]
         L.pkv_mfma_peak.restype = I
         _lib = L
@@ -543,6 +545,20 @@ def stream_read(buf, sink, workgroups=4096, nontemporal=True, stream=None):
                              _stream(stream))
     if rc:
         raise PkvError(rc, "pkv_stream_read")
+
+
+def stream_copy(src, dst, workgroups=8192, stream=None):
+    """Measurement aid: one plain device copy of `src` into `dst` (same
+    byte size, contiguous, not overlapping; pkv_stream_copy)."""
+    lib = _load()
+    _need_gpu(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if (dst.numel() * dst.element_size() != nbytes or not src.is_contiguous()
+            or not dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous and of the same byte size")
+    rc = lib.pkv_stream_copy(_ptr(src), _ptr(dst), nbytes, int(workgroups), _stream(stream))
+    if rc:
+        raise PkvError(rc, "pkv_stream_copy")
 
 
 def mfma_peak(sink, workgroups, iters, stream=None):

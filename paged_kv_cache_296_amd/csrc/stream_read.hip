@@ -1,6 +1,6 @@
-// Measurement aid: a plain streaming read of one device buffer, the
+// Measurement aids: a plain streaming read of one device buffer, the
 // practical HBM read ceiling that the decode kernels' K/V bandwidth is set
-// against (the 8 TB/s figure is the part's specification; no kernel reaches
+// against, and a plain copy (further down), the ceiling for the cache write (the 8 TB/s figure is the part's specification; no kernel reaches
 // it).  Every lane reads 16-byte words, four in flight, grid-stride over
 // windows of at most 1 GiB (one buffer descriptor each), with the same
 // non-temporal cache hint the decode kernels put on their K/V loads, or
@@ -43,6 +43,31 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const char* __restrict
     sink[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Plain device copy of `bytes` bytes (< 2 GiB), the same loads plus 16-byte
+// stores, eight words in flight per lane: the practical ceiling for kernels
+// that move every byte they read (the paged cache write).
+__global__ __launch_bounds__(256) void stream_copy_kernel(const char* __restrict__ src,
+                                                          char* __restrict__ dst, int bytes) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dst, (short)0, bytes, 0x00020000);
+  const int n = bytes / 16, stride = gridDim.x * 256;
+  int i = blockIdx.x * 256 + threadIdx.x;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (i + u * stride), 0, 2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, 16 * (i + u * stride), 0, 0);
+  }
+  for (; i < n; i += stride)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, 16 * i, 0, 2),
+                                           rd, 16 * i, 0, 0);
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -59,5 +84,16 @@ extern "C" int pkv_stream_read(const void* buf, size_t bytes, void* sink, int wo
   else
     hipLaunchKernelGGL(pkv::stream_read_kernel<0>, grid, block, 0, (hipStream_t)stream,
                        (const char*)buf, (long long)bytes, (pkv::u32x4*)sink);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+extern "C" int pkv_stream_copy(const void* src, void* dst, size_t bytes, int workgroups,
+                               void* stream) {
+  if (src == nullptr || dst == nullptr || workgroups <= 0 || workgroups > 65535 ||
+      bytes % 16 != 0 || bytes >= ((size_t)1 << 31))
+    return PKV_EINVAL;
+  if (bytes == 0) return PKV_OK;
+  hipLaunchKernelGGL(pkv::stream_copy_kernel, dim3((unsigned)workgroups), dim3(256), 0,
+                     (hipStream_t)stream, (const char*)src, (char*)dst, (int)bytes);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
