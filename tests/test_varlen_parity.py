@@ -4,8 +4,9 @@ Covers the HF page's worked example (a request with no key, one with a single
 key, one with seven), the 16-sequence prefill batch at full size (every 8th row
 of each request and both edges of every q tile for the oracle), the 8 x 1024 prefill of the mixed step, and small cases
 with ragged tails, empty requests, head_dim 64/128, group sizes 1..8 (each
-workgroup packing of q heads), negative / zero / large softmax scales and
-scores whose row max keeps moving across key tiles; batches on both sides of
+workgroup packing of q heads), negative / zero / large softmax scales,
+scores whose row max keeps moving across key tiles and scores placed just
+under and over the point where the kernel moves its softmax reference; batches on both sides of
 the persistent kernel's limits (256 requests ranked longest first, 960 in
 all; the grid form serves larger batches), and bit-identical results across
 those boundaries.
@@ -113,6 +114,34 @@ def test_rising_and_falling_scores_across_tiles():
     ramp = torch.linspace(0.05, 3.0, n, device=DEV)
     ramp[n // 2:] = ramp[n // 2:].flip(0)
     case.k.mul_(ramp.view(1, n, 1, 1).to(case.k.dtype))
+    run_case(case)
+
+
+def test_lazy_reference_thresholds():
+    """Scores placed so that a later key tile passes the running softmax
+    reference by chosen amounts (log2 units, after bf16 rounding of q): one
+    key 6, 10, 14 or 40 above it, or a whole tile 5, 7.89 or 8.07 above it --
+    a lane's sum of its 32 exponentials just under and just over 32 * 2^8.
+    Exponentials the kernel keeps (up to 2^13) and those it takes again after
+    moving the reference must both match the oracle."""
+    lq, lk = [4, 3], [300, 256]
+    case = workloads.make_varlen(seed=4600, dtype="bf16", batch=2, num_heads=4, num_kv_heads=1,
+                                 head_dim=128, q_lengths=lq, k_lengths=lk, device=DEV,
+                                 softmax_scale=1.0)
+    log2e = 1.4426950408889634
+    q = torch.zeros_like(case.q, dtype=torch.float32)
+    k = case.k.float()
+    k[..., 0] = 1.0
+    # request 0: key 100 (second tile) scores d above the first tile's keys
+    k[0, 100, 0, 0] = 2.0
+    for i, d in enumerate([6.0, 10.0, 14.0, 40.0]):
+        q[0, i, :, 0] = d / log2e
+    # request 1: keys 128..191 (third tile) all d above the others
+    k[0, lk[0] + 128:lk[0] + 192, 0, 0] = 2.0
+    for i, d in enumerate([5.0, 7.9, 8.1]):
+        q[0, lq[0] + i, :, 0] = d / log2e
+    case.q.copy_(q.to(case.q.dtype))
+    case.k.copy_(k.to(case.k.dtype))
     run_case(case)
 
 
