@@ -256,10 +256,30 @@ __device__ __forceinline__ void exp_pair(const f32x16 (&s)[2], int e, float c, f
   pw[mt][r >> 1] = w;
 }
 
+// exp_pair in two halves, for a software pipeline: the exponentials of a
+// pair, then (one MFMA later) their bf16 packing and row sum, so that no
+// instruction waits on a transcendental result issued just before it.
+__device__ __forceinline__ void exp_pair_start(const f32x16 (&s)[2], int e, float c, float neg_m,
+                                               float& p0, float& p1) {
+  const int mt = e >> 3, r = 2 * (e & 7);
+  p0 = fast_exp2(fmaf(s[mt][r], c, neg_m));
+  p1 = fast_exp2(fmaf(s[mt][r + 1], c, neg_m));
+}
+__device__ __forceinline__ void exp_pair_finish(float p0, float p1, int e, float& psum,
+                                                u32 (&pw)[2][8]) {
+  const int mt = e >> 3, r = 2 * (e & 7);
+  const u32 w = pack_bf16x2(p0, p1);
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, psum, false);
+  pw[mt][r >> 1] = w;
+}
+
 // S^T of the next tile (16 MFMAs, K operand read four steps ahead) with the
 // exponentials of the current tile spread between them, so that the matrix
-// core and the vector ALU of one wave work at the same time.  The scheduling
-// fences keep this interleaving and keep the K reads from all being hoisted.
+// core and the vector ALU of one wave work at the same time; each slot
+// packs and sums the pairs whose exponentials the slot before started.  The
+// scheduling fences keep this interleaving and keep the K reads from all
+// being hoisted.
 template <int D>
 __device__ __forceinline__ void qk_and_exp(u32 kt, const u32x4* qr, const u32* koff,
                                            f32x16 (&sn)[2], const f32x16 (&sc)[2], float c,
@@ -274,16 +294,23 @@ __device__ __forceinline__ void qk_and_exp(u32 kt, const u32x4* qr, const u32* k
   u32x4 kf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) kf[i] = k_operand<D>(kt, koff, i);
+  float p0[EPS], p1[EPS];
 #pragma unroll
   for (int i = 0; i < NQK; ++i) {
     sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[i & 3]),
                                                         __builtin_bit_cast(bf16x8, qr[i >> 1]),
                                                         sn[i & 1], 0, 0, 0);
     if (i + 4 < NQK) kf[i & 3] = k_operand<D>(kt, koff, i + 4);
+    if (i > 0) {
 #pragma unroll
-    for (int e = 0; e < EPS; ++e) exp_pair(sc, EPS * i + e, c, neg_m, psum, pw);
+      for (int e = 0; e < EPS; ++e) exp_pair_finish(p0[e], p1[e], EPS * (i - 1) + e, psum, pw);
+    }
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) exp_pair_start(sc, EPS * i + e, c, neg_m, p0[e], p1[e]);
     __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int e = 0; e < EPS; ++e) exp_pair_finish(p0[e], p1[e], EPS * (NQK - 1) + e, psum, pw);
 }
 
 // S^T of one tile alone (the first tile).
