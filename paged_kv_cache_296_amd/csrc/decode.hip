@@ -304,10 +304,15 @@ __device__ __forceinline__ void store_out(char* dst, const float* o) {
 // the slot of its first partition.  (A global store in mid-stream would make
 // every later tile wait also wait for the store's acknowledgement: the
 // vector-memory counter retires loads and stores in order.)
-template <bool BF16, int D, int BS, int CPOL>
+// `started` runs once per unit, right after the unit's first tile loads are
+// issued (or where it gives up early): the persistent kernel takes its next
+// ticket there, so that the ticket atomic -- slow on its one contended
+// counter -- sits behind those loads in the in-order vector-memory counter
+// instead of ahead of them.
+template <bool BF16, int D, int BS, int CPOL, class Started>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, float* run_w,
                                             int lane, int seq, int p0, int nparts, int L, int kvh,
-                                            int hc) {
+                                            int hc, Started&& started) {
   using S = Shape<BF16, D>;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int P = a.part_tokens;
@@ -350,6 +355,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
 
   if (L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS) {
     fail(kErrSpan);
+    started();
     return;
   }
   const int te = min(tb + nparts * P, Lp);
@@ -366,6 +372,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
   }
   if (__any(bad)) {
     fail(kErrBlock);
+    started();
     return;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -528,6 +535,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
       // it conservative
       issue(0, b0);
       issue(min(1, last), b1);
+      started();
       int t = 0;
       // sched_barrier keeps the compiler from hoisting work on a tile whose
       // loads were just issued above the compute of the tile before it
@@ -556,6 +564,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
       // a new token that starts a partition of its own: close the last
       // partition of cached tokens first
       if (owns_new && L % P == 0) flush(L / P - 1);
+    } else {
+      started();
     }
     if (owns_new) {
       new_token_tile<BF16, S>(b1, lane, knew, vnew);
@@ -568,7 +578,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
 
 // Persistent per-partition kernel: each wave takes units by ticket from the
 // work list the plan kernel built, prefetching its next ticket while it
-// works, until the list is exhausted.  No workgroup is launched for an empty
+// works (the atomic goes out right after the unit's first tile loads: ahead
+// of them, the in-order vector-memory counter made the first tile wait for
+// it -- 64 GQA-4 sequences 148 -> 141 us per step), until the list is
+// exhausted.  No workgroup is launched for an empty
 // partition and the tail drains on the shortest units.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
@@ -594,8 +607,7 @@ void decode_partial_kernel(DecodeArgs a) {
     __syncthreads();
     const unsigned T = (unsigned)__builtin_amdgcn_readfirstlane(s_ticket[it & 1]);
     if ((unsigned long long)T * kWaves >= total) break;
-    if (wave == 0 && lane == 0) ticket = atomicAdd(&a.ctrl[0], 1);
-    const unsigned u = T * kWaves + wave;
+    const unsigned u = T * kWaves + wave;  // wave 0's unit always exists
     if (u >= total) continue;
     const int4 item = a.items[u / (unsigned)per_item];
     const int r = (int)(u % (unsigned)per_item);
@@ -603,7 +615,9 @@ void decode_partial_kernel(DecodeArgs a) {
     decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane,
                              __builtin_amdgcn_readfirstlane(item.x),
                              packed >> 8, packed & 255, __builtin_amdgcn_readfirstlane(item.z),
-                             r / a.head_chunks, r % a.head_chunks);
+                             r / a.head_chunks, r % a.head_chunks, [&]() {
+                               if (wave == 0 && lane == 0) ticket = atomicAdd(&a.ctrl[0], 1);
+                             });
   }
 }
 
@@ -630,7 +644,8 @@ void decode_direct_kernel(DecodeArgs a) {
   const int Lp = L + a.has_new;
   const bool bad = L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS;
   if (part > 0 && (bad || part * a.part_tokens >= Lp)) return;
-  decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh, hc);
+  decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh,
+                                        hc, []() {});
 }
 
 // Work list for the persistent kernel, one workgroup.  Every sequence's
