@@ -304,11 +304,12 @@ __device__ __forceinline__ void store_out(char* dst, const float* o) {
 // the slot of its first partition.  (A global store in mid-stream would make
 // every later tile wait also wait for the store's acknowledgement: the
 // vector-memory counter retires loads and stores in order.)
-// `started` runs once per unit, right after the unit's first tile loads are
+// `started` runs once per unit, right after the unit's last tile loads are
 // issued (or where it gives up early): the persistent kernel takes its next
 // ticket there, so that the ticket atomic -- slow on its one contended
-// counter -- sits behind those loads in the in-order vector-memory counter
-// instead of ahead of them.
+// counter -- sits behind every load of the unit in the in-order
+// vector-memory counter, where no wait of the unit waits for it; it has the
+// unit's last tiles to complete before the next ticket exchange needs it.
 template <bool BF16, int D, int BS, int CPOL, class Started>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, float* run_w,
                                             int lane, int seq, int p0, int nparts, int L, int kvh,
@@ -535,7 +536,6 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
       // it conservative
       issue(0, b0);
       issue(min(1, last), b1);
-      started();
       int t = 0;
       // sched_barrier keeps the compiler from hoisting work on a tile whose
       // loads were just issued above the compute of the tile before it
@@ -558,6 +558,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
       if (rem >= 3) issue(t + 2, b2);
       compute(t, b0);
       if (rem >= 4) issue(t + 3, b0);
+      started();  // every load of the unit is out
       if (rem >= 2) compute(t + 1, b1);
       if (rem >= 3) compute(t + 2, b2);
       if (rem >= 4) compute(t + 3, b0);
@@ -578,10 +579,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
 
 // Persistent per-partition kernel: each wave takes units by ticket from the
 // work list the plan kernel built, prefetching its next ticket while it
-// works (the atomic goes out right after the unit's first tile loads: ahead
-// of them, the in-order vector-memory counter made the first tile wait for
-// it -- 64 GQA-4 sequences 148 -> 141 us per step), until the list is
-// exhausted.  No workgroup is launched for an empty
+// works (the atomic goes out after the unit's last tile loads: ahead of its
+// first ones, the in-order vector-memory counter made the first tile wait
+// for it, and ahead of later ones, the later tiles -- step time 148 -> 141
+// us on 64 GQA-4 sequences, 1604 -> 1565 us on the long-context batch),
+// until the list is exhausted.  No workgroup is launched for an empty
 // partition and the tail drains on the shortest units.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
