@@ -18,24 +18,36 @@ bool decode_shape_ok(int head_dim, int block_size) {
   return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
 }
 
-// Library choice of partition length: 512 tokens, halved (down to 128) while
-// the expected units -- sequences averaging half their table span -- would
-// not give each of the 2048 resident waves of the per-partition kernel two
-// of them; the whole row when it is shorter.  Always a block multiple within
-// the LDS slice.  Measured with the last-level cache flushed before each
-// step, GQA-4 batches of 512..4096 tokens at 32 / 64 / 128 / 256 sequences:
-// 128-token partitions 92 / 165 / 272 / 472 us, 256: 127 / 149 / 272 / 466,
-// 512: 122 / 202 / 253 / 491, 1024: 123 / 204 / 346 / 459; this rule picks
-// 128 / 256 / 512 / 512 (the previous target of one unit per SIMD picked 512
-// for 64 sequences).
+// Library choice of partition length: 512 tokens when the batch has enough
+// units for that (each row assumed to average half its table span), else
+// the length at which the expected units give each of the 2048 resident
+// waves of the per-partition kernel about 1.75 of them, rounded up to a
+// multiple of 64 tokens, at least 128; the whole row when it is shorter.
+// Always a block multiple within the LDS slice.  Measured with the
+// last-level cache flushed before each step, GQA-4 batches of 512..4096
+// tokens, whole step: 32 sequences 83.2 (128-token partitions) / 77.0 (192)
+// / 72.6 (384) us, 64 sequences 136.3 (256) / 130.5 (320) / 132.6 (384) /
+// 137.0 (608) us, 128 sequences 235.8 (512) / 233.7 (640) us; the optimum
+// moves in jumps with the drawn lengths (how the last round of units falls
+// on the resident waves), which the host cannot see -- this rule picks 192 /
+// 320 / 512 (the previous one, halving 512 while fewer than two units per
+// wave were expected, picked 128 / 256 / 512).
 int choose_partition(int batch, int num_kv_heads, int head_chunks, int block_size,
                      int max_blocks_per_seq) {
   const long long span = (long long)max_blocks_per_seq * block_size;
   const long long cap = (long long)kMaxPartitionBlocks * block_size;
   const long long base_units = (long long)batch * num_kv_heads * head_chunks;
-  const long long floor_p = block_size > 128 ? block_size : 128;
+  const double target = 1.75 * 2048;  // units
+  const double half = (double)span / 2;
   long long p = 512;
-  while (p / 2 >= floor_p && base_units * ((span / 2 + p - 1) / p) < 4096) p /= 2;
+  // expected units at partition p: base_units * (half / p + 0.5)
+  if ((double)base_units * (half / 512 + 0.5) < target) {
+    const double per_row = target / (double)base_units - 0.5;  // partitions per row
+    const double want = half / per_row;
+    p = ((long long)want + 63) / 64 * 64;
+    if (p < 128) p = 128;
+    if (p > 512) p = 512;
+  }
   if (p > cap) p = cap;
   p -= p % block_size;
   if (p < block_size) p = block_size;

@@ -143,22 +143,25 @@ def test_product_path_refuses_cpu_tensors(pkv):
 
 
 def test_library_partition_rule(pkv):
-    # 512 tokens when the batch gives every resident wave (2048) two units
-    # (the long-context and mixed-step shapes), whatever the row span beyond it
+    # 512 tokens when the batch then has about 1.75 units per resident wave
+    # (2048 waves; rows assumed to average half their span) or more: the
+    # long-context and mixed-step shapes, whatever the row span beyond it
     assert pkv.decode_partition_tokens(256, 64, 8, 128, 16, 2048, 0) == 512
     assert pkv.decode_partition_tokens(512, 32, 8, 128, 16, 513, 0) == 512
     assert pkv.decode_partition_tokens(128, 32, 8, 128, 16, 256, 0) == 512
-    # fewer: halved until they do -- 64 GQA-4 sequences of up to 4096 tokens
-    # get 256, 32 of them 128
-    assert pkv.decode_partition_tokens(64, 32, 8, 128, 16, 256, 0) == 256
-    assert pkv.decode_partition_tokens(32, 32, 8, 128, 16, 256, 0) == 128
+    # fewer: the length that gives that many, rounded up to 64 tokens --
+    # 64 GQA-4 sequences of up to 4096 tokens get 320, 48 of them 256, 32
+    # of them 192
+    assert pkv.decode_partition_tokens(64, 32, 8, 128, 16, 256, 0) == 320
+    assert pkv.decode_partition_tokens(48, 32, 8, 128, 16, 256, 0) == 256
+    assert pkv.decode_partition_tokens(32, 32, 8, 128, 16, 256, 0) == 192
     # a row shorter than the partition: one pass over the whole row when
     # that gives enough units
     assert pkv.decode_partition_tokens(1024, 32, 8, 128, 16, 20, 0) == 320
     # ... else split: 64 x 8 one-pass units become 128-token parts
     assert pkv.decode_partition_tokens(64, 32, 8, 128, 16, 20, 0) == 128
-    # halved, but never below 128 tokens
-    assert pkv.decode_partition_tokens(1, 8, 8, 128, 16, 8192, 0) == 128
+    # never below 128 tokens (one long sequence: 192 here)
+    assert pkv.decode_partition_tokens(1, 8, 8, 128, 16, 8192, 0) == 192
     assert pkv.decode_partition_tokens(1, 8, 2, 128, 16, 512, 0) == 128
     assert pkv.decode_partition_tokens(1, 8, 1, 128, 32, 4096, 0) == 128
     # an explicit partition is kept as given

@@ -320,6 +320,18 @@ def test_runs_of_partitions(pt):
     run_case(case, "bf16")
 
 
+def test_work_list_past_the_cached_chunks():
+    """4500 sequences: the plan kernel keeps the lengths of the first 4096
+    (four chunks of 1024) in registers between its passes and reads the rest
+    again; every sequence is compared with the oracle."""
+    lengths = np.random.default_rng(4150).integers(0, 100, size=4500)
+    lengths[[0, 4095, 4096, 4499]] = [0, 99, 1, 64]
+    case = workloads.make_decode(seed=4150, dtype="bf16", batch=4500, num_heads=8,
+                                 num_kv_heads=2, head_dim=128, block_size=16, lengths=lengths,
+                                 num_blocks=40000, append=True, partition_tokens=16, device=DEV)
+    run_case(case, "bf16")
+
+
 @pytest.mark.parametrize("pt", [16, 48])
 def test_large_batch_work_list(pt):
     """More than 1024 sequences through the persistent kernel: the work list
