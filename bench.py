@@ -116,11 +116,14 @@ class Flusher:
 
 
 def time_decode(pkv, torch, case, steps, warmup, flush=None):
-    """Warmup, then `steps` timed decode steps (plan + per-partition kernel +
-    merge).  With `flush`, the cache is flushed before each step and each step
-    is timed alone by events; without, the steps run back to back and the
-    wall clock is taken too.  Returns dict(step_ms, part_ms, merge_ms,
-    wall_ms)."""
+    """Warmup, then `steps` timed decode steps, each one `decode` call (plan,
+    per-partition kernel, merge) between two HIP events, as a caller runs it;
+    then the same steps again as the two phase calls with an event between
+    them, for the per-kernel split only (an event between the kernels costs
+    a few microseconds of its own, so it stays out of the step time).  With
+    `flush`, the cache is flushed before each step; without, the steps run
+    back to back and the wall clock of the whole-call loop is taken too.
+    Returns dict(step_ms, part_ms, merge_ms, wall_ms, out)."""
     out = torch.empty_like(case.q)
     B, _, Hq, D = case.q.shape
     NB, bs, Hkv, _ = case.k_cache.shape
@@ -132,30 +135,34 @@ def time_decode(pkv, torch, case, steps, warmup, flush=None):
     args = (case.q, case.k_cache, case.v_cache, case.block_table, case.cache_seqlens,
             case.k_new, case.v_new)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        pkv.decode_partials(*args, **kw)
-        if ev is not None:
-            ev[1].record()
-        pkv.decode_merge(*args, **kw)
-        if ev is not None:
-            ev[2].record()
+    def whole():
+        pkv.decode(*args, **kw)
 
-    for _ in range(warmup):
-        if flush is not None:
-            flush()
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        if flush is not None:
-            flush()
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    return {"step_ms": sum(e[0].elapsed_time(e[2]) for e in evs) / steps,
+    def split(ev):
+        pkv.decode_partials(*args, **kw)
+        ev.record()
+        pkv.decode_merge(*args, **kw)
+
+    def run(timed_step, nev):
+        for _ in range(warmup):
+            if flush is not None:
+                flush()
+            whole()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush is not None:
+                flush()
+            evs[i][0].record()
+            timed_step(evs[i])
+            evs[i][-1].record()
+        torch.cuda.synchronize()
+        return evs, (time.perf_counter() - t0) * 1e3 / steps
+
+    evw, wall_ms = run(lambda ev: whole(), 2)
+    evs, _ = run(lambda ev: split(ev[1]), 3)
+    return {"step_ms": sum(e[0].elapsed_time(e[1]) for e in evw) / steps,
             "part_ms": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
             "merge_ms": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
             "wall_ms": None if flush is not None else wall_ms, "out": out}
