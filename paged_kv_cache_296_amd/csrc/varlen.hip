@@ -336,26 +336,30 @@ __device__ __forceinline__ void qk_only(u32 kt, const u32x4* qr, const u32* koff
   }
 }
 
-// O^T += V^T P^T over the tile's 64 keys.  16 keys per step: this lane's P^T
-// operand holds keys 16 kc + 4 hh + {0..3} and 16 kc + 8 + 4 hh + {0..3}, and
-// the two transposing reads fetch V^T for exactly those keys.  The reads run
-// two MFMAs ahead.
+// V^T operand i of the tile's P.V product: keys 16 kc .. 16 kc + 15 (kc =
+// i / DT) of dims 32 d .. 32 d + 31 (d = i % DT).  This lane's P^T operand
+// holds keys 16 kc + 4 hh + {0..3} and 16 kc + 8 + 4 hh + {0..3}, and the two
+// transposing reads fetch V^T for exactly those keys.
+template <int D>
+__device__ __forceinline__ i16x8 v_operand(u32 vt, const u32* voff, int i) {
+  using G = Geo<D>;
+  const int kc = i / G::DT, d = i % G::DT;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      lds_at<lds_i16x4>(vt + voff[2 * d] + 16 * kc * G::ROWB));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      lds_at<lds_i16x4>(vt + voff[2 * d + 1] + 16 * kc * G::ROWB));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// O^T += V^T P^T over the tile's 64 keys, 16 keys per step.  vf: operands 0
+// and 1, read by the caller (in the tile loop before the overflow check, so
+// that their latency runs under the last QK^T MFMAs); the reads run two
+// MFMAs ahead.
 template <int D>
 __device__ __forceinline__ void pv(u32 vt, const u32* voff, const u32 (&pw)[2][8],
-                                   f32x16* acc) {
+                                   f32x16* acc, i16x8 (&vf)[2]) {
   using G = Geo<D>;
   constexpr int NPV = 4 * G::DT;
-  auto vread = [&](int i) {
-    const int kc = i / G::DT, d = i % G::DT;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        lds_at<lds_i16x4>(vt + voff[2 * d] + 16 * kc * G::ROWB));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        lds_at<lds_i16x4>(vt + voff[2 * d + 1] + 16 * kc * G::ROWB));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  i16x8 vf[2];
-  vf[0] = vread(0);
-  vf[1] = vread(1);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     const int kc = i / G::DT, d = i % G::DT;
@@ -364,7 +368,7 @@ __device__ __forceinline__ void pv(u32 vt, const u32* voff, const u32 (&pw)[2][8
     acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[i & 1]),
                                                      __builtin_bit_cast(bf16x8, pf), acc[d],
                                                      0, 0, 0);
-    if (i + 2 < NPV) vf[i & 1] = vread(i + 2);
+    if (i + 2 < NPV) vf[i & 1] = v_operand<D>(vt, voff, i + 2);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -554,6 +558,12 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
     // 2-3 % on short items at head_dim 128, the 16-request batch even)
     __builtin_amdgcn_s_setprio(1);
     qk_and_exp<D>(kofs(j + 1), qr, koff, sn, sc, c, -m_ref, psum, pw);
+    // P.V's first two V^T operands go out here, before the overflow check,
+    // rather than at the start of P.V: their LDS latency then runs under the
+    // last QK^T MFMAs (+1.4 to +1.9 % on the 16-request batch, uniform
+    // batches and head_dim 64, +0.6 to +1 % on the mixed-step prefill; two
+    // boxes, two rounds each)
+    i16x8 vf[2] = {v_operand<D>(vofs(j), voff, 0), v_operand<D>(vofs(j), voff, 1)};
     __builtin_amdgcn_s_setprio(0);
     // the exponentials were taken against the current reference before the
     // tile's max is known; the lane's sum of its 32 of them bounds each, so
@@ -567,7 +577,7 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
       for (int e = 0; e < 16; ++e) exp_pair(sc, e, c, neg_m, psum, pw);
     }
     l_run += psum;
-    pv<D>(vofs(j), voff, pw, acc);
+    pv<D>(vofs(j), voff, pw, acc, vf);
   };
   if (nk > 0) {
     issue(kg, 0, kbuf(0));
@@ -602,7 +612,8 @@ __device__ __forceinline__ void varlen_item(const VarlenArgs& a, int qt, int hy,
 #pragma unroll
       for (int e = 0; e < 16; ++e) exp_pair(sa, e, c, neg_m, psum, pw);
       l_run += psum;
-      pv<D>(vofs(j), voff, pw, acc);
+      i16x8 vf[2] = {v_operand<D>(vofs(j), voff, 0), v_operand<D>(vofs(j), voff, 1)};
+      pv<D>(vofs(j), voff, pw, acc, vf);
     }
   }
 
