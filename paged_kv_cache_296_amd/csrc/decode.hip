@@ -652,8 +652,10 @@ void decode_direct_kernel(DecodeArgs a) {
 
 // Work list for the persistent kernel, one workgroup.  Every sequence's
 // partitions are cut into runs of R consecutive partitions (R chosen so that
-// there are at least about three units per resident wave, and at most
-// a.max_run).  The runs that do not hold a sequence's end are all R full
+// there are at least about two units per resident wave, and at most
+// a.max_run: every unit start costs a wave several dependent memory round
+// trips with no tile in flight, so fewer, longer units pay while the tail
+// still balances).  The runs that do not hold a sequence's end are all R full
 // partitions long and come first, in sequence order; then each sequence's
 // last run, longest first (bucketed by token count), so that the list ends
 // on the shortest units and the waves run dry together.  A sequence with
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a, int blo
   int total_parts;
   block_exclusive_scan(my, s_w, total_parts);
   const long long units = (long long)total_parts * a.num_kv_heads * a.head_chunks;
-  long long rr = units / (3LL * a.resident_waves);
+  long long rr = units / (2LL * a.resident_waves);
   const int R = (int)(rr < 1 ? 1 : (rr > a.max_run ? a.max_run : rr));
   if (tid == 0) a.ctrl[0] = 0;
   const long long rp = (long long)R * a.part_tokens;  // tokens of a full run

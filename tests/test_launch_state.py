@@ -66,7 +66,8 @@ def test_decode_plan_not_changed_by_an_earlier_fp32_call():
     R, cus = _plan_run_length(fp32_first=True)
     units = 72 * 32 * 8
     resident_waves = 2 * cus * 4           # bf16 head_dim 128: 2 workgroups of 4 waves per CU
-    want = max(1, min(8, units // (3 * resident_waves)))
+    # the plan aims at about two units per resident wave, at most 8 partitions a run
+    want = max(1, min(8, units // (2 * resident_waves)))
     assert R == want, (R, want, cus)
     R2, _ = _plan_run_length(fp32_first=False)
     assert R2 == R
