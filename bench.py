@@ -194,11 +194,11 @@ def varlen_call(pkv, case, out):
 
 
 def stream_peak(pkv, torch, dev, steps=5):
-    """pkv_stream_read over 8 GiB (32x the last-level cache), with and
-    without the non-temporal hint: GB/s of the mean call."""
+    """pkv_stream_read over 8 GiB (32x the last-level cache; 1 MB per wave),
+    with and without the non-temporal hint: GB/s of the mean call."""
     nbytes = 8 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    wgs = 4096
+    wgs = 2048
     sink = torch.empty(wgs * 4096, dtype=torch.uint8, device=dev)
     res = {"bytes": nbytes, "workgroups": wgs}
     for name, nt in (("nontemporal", True), ("default", False)):

@@ -415,13 +415,15 @@ int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
 /* ------------------------------------------------------ measurement aid
  *
  * Reads `bytes` bytes of the device buffer `buf` once, as a plain stream
- * (16-byte loads, grid-stride, `workgroups` workgroups of 256 lanes), with
- * the non-temporal cache hint the decode kernels put on their K/V loads
- * (nontemporal = 1) or none (0).  It computes nothing; timing it gives the
- * practical HBM read ceiling the decode bandwidth is compared with.  `sink`
- * is device memory of workgroups * 4096 bytes that the kernel may write (in
- * practice it writes nothing).  bytes must be a multiple of 16; workgroups in
- * 1 .. 65535.  PKV_EINVAL on bad arguments.
+ * (`workgroups` workgroups of four waves; each wave reads one contiguous
+ * chunk of bytes / (4 * workgroups) bytes, rounded up to 1 KiB, in 16-byte
+ * loads, at most two waves per SIMD), with the non-temporal cache hint the
+ * decode kernels put on their K/V loads (nontemporal = 1) or none (0).  It
+ * computes nothing; timing it gives the practical HBM read ceiling the decode
+ * bandwidth is compared with.  `sink` is device memory of workgroups * 4096
+ * bytes that the kernel may write (in practice it writes nothing).  bytes
+ * must be a multiple of 16; workgroups in 1 .. 65535; a wave's chunk may not
+ * exceed 1 GiB.  PKV_EINVAL on bad arguments.
  */
 int pkv_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, int nontemporal,
                     void* stream);

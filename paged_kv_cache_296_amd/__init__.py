@@ -532,7 +532,7 @@ def copy_blocks(k_cache, v_cache, src, dst, *, err_flag=None, stream=None):
         raise PkvError(rc, "pkv_copy_blocks")
 
 
-def stream_read(buf, sink, workgroups=4096, nontemporal=True, stream=None):
+def stream_read(buf, sink, workgroups=2048, nontemporal=True, stream=None):
     """Measurement aid: one plain streaming read of the device tensor `buf`
     (pkv_stream_read).  `sink` is a device tensor of at least workgroups *
     4096 bytes."""

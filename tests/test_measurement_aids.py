@@ -45,6 +45,7 @@ def test_bad_arguments_are_refused():
     assert lib.pkv_stream_copy(None, p, 512, 4, None) == pkv.EINVAL
     assert lib.pkv_stream_read(p, 24, p, 4, 1, None) == pkv.EINVAL
     assert lib.pkv_stream_read(p, 512, p, 4, 2, None) == pkv.EINVAL           # hint is 0 or 1
+    assert lib.pkv_stream_read(p, 8 << 30, p, 1, 1, None) == pkv.EINVAL       # 2 GiB per wave
     assert lib.pkv_mfma_peak(p, 0, 10, None) == pkv.EINVAL
     assert lib.pkv_mfma_peak(p, 4, -1, None) == pkv.EINVAL
     assert lib.pkv_mfma_peak(None, 4, 10, None) == pkv.EINVAL
