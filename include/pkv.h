@@ -417,7 +417,7 @@ int pkv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
  * Reads `bytes` bytes of the device buffer `buf` once, as a plain stream
  * (`workgroups` workgroups of four waves; each wave reads one contiguous
  * chunk of bytes / (4 * workgroups) bytes, rounded up to 1 KiB, in 16-byte
- * loads, at most two waves per SIMD), with the non-temporal cache hint the
+ * loads), with the non-temporal cache hint the
  * decode kernels put on their K/V loads (nontemporal = 1) or none (0).  It
  * computes nothing; timing it gives the practical HBM read ceiling the decode
  * bandwidth is compared with.  `sink` is device memory of workgroups * 4096

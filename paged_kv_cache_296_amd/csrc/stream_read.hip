@@ -5,10 +5,11 @@
 // In the read each wave streams one contiguous chunk of the buffer (the
 // chunks tile it in wave order) in bursts of four 16-byte loads per lane,
 // with the same non-temporal cache hint the decode kernels put on their K/V
-// loads, or none, at most two waves per SIMD.  Against the previous form
-// (every lane grid-stride over the whole buffer, four loads in flight), on
-// one box: 8 GiB read 6.50 -> 7.14 TB/s (1 MB per wave, 2048 workgroups; the
-// grid-stride form peaked at 6.75 with 8192).  The grid-stride sweep keeps
+// loads, or none.  Against the previous form (every lane grid-stride over
+// the whole buffer, four loads in flight), on one box: 8 GiB read 6.50 ->
+// 7.14 TB/s (2048 workgroups, which at this kernel's register use are all
+// resident at once, 1 MB per wave; the grid-stride form peaked at 6.75 with
+// 8192).  The grid-stride sweep keeps
 // every workgroup's requests inside one narrow window of the buffer at a
 // time.  The copy keeps the grid-stride form, which stays the faster one at
 // the cache write's size (83 MB: 5.1-5.2 against at most 4.75 TB/s).
@@ -37,8 +38,7 @@ __device__ __forceinline__ int wave_chunk(long long bytes, long long chunk, long
 }
 
 template <int CPOL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void stream_read_kernel(const char* __restrict__ p, long long bytes, long long chunk,
+__global__ __launch_bounds__(256) void stream_read_kernel(const char* __restrict__ p, long long bytes, long long chunk,
                         u32x4* sink) {
   u32x4 acc = {0u, 0u, 0u, 0u};
   long long b0;
