@@ -7,21 +7,34 @@
 // sequence b and is copied, bit for bit, to slot p mod block_size of
 // physical block block_table[b][p / block_size], for K and for V.
 //
-// How: one wave per 2 consecutive packed rows.  The 64 lanes move the rows'
+// How: one wave per 2 consecutive packed rows; the 64 lanes move a row's
 // Hkv * D elements (2 KB per row of K at 8 kv heads x 128 bf16) in 16-byte
-// pieces, issuing the loads of both rows of K and V first -- each lane has 8
-// loads in flight -- and only then locating the rows' slots: everything
-// that locates a row -- its request (one load of cu per lane and a ballot,
-// or a binary search for large batches), its token position, its table
-// entry -- is wave-uniform and runs on the scalar unit, three dependent
-// round trips that the loads now overlap (39.0-39.7 -> 36.2-36.4 us on the
-// 16-request prefill batch; 1 and 4 rows per wave 39.6 and 37.5 us).  A row is contiguous at both ends (a
-// token row of the cache is [Hkv][D] like a packed row), so both sides are
-// coalesced.  The packed rows are read once, with the non-temporal hint
-// (measured 28 % faster than plain loads on the 16-request prefill batch:
-// 55.5 -> 40.0 us with the last-level cache flushed before each call; the
-// same hint on the stores changed nothing).  HBM bound: 2 reads + 2 writes
-// of the row per packed row.
+// pieces, P pieces per lane (P = row bytes / 1 KB rounded up, at most 4; a
+// template parameter).  A row is contiguous at both ends (a token row of the
+// cache is [Hkv][D] like a packed row), so both sides are coalesced.  The
+// order of a wave's memory traffic is what sets the time: on gfx9 the
+// vector-memory counter retires loads in issue order, so any vector load
+// issued after the rows' loads and waited on waits for all of them.  So:
+//   1. each lane loads cu[lane] and start[lane] (requests up to 63), the
+//      only vector loads besides the rows';
+//   2. the rows' loads go out, all of them unconditionally, through buffer
+//      descriptors that bound them to the wave's rows (a lane past the row
+//      end gets an out-of-range offset: no memory access);
+//   3. waiting only for step 1, a ballot on cu gives each row's request,
+//      lane reads give its cu and start, and the table entry comes through
+//      the scalar cache (more than 63 requests: a binary search there too),
+//      all while the rows are in flight;
+//   4. the stores, through one descriptor per destination row whose range
+//      is empty when the row has no valid slot.
+// Against the previous form (conditional global loads, and lookups issued as
+// vector loads after the rows: four dependent round trips that each waited
+// for every row load), on the 16-request prefill batch (167 MB moved) with
+// the last-level cache cold, same box: 33.6-33.7 -> 31.0-31.1 us by events
+// (5.37 TB/s; a plain copy of the same bytes 29.7-30.0 us).  The packed rows
+// are read once, with the non-temporal hint (measured 28 % faster than plain
+// loads on that batch); the same hint on the stores measured 8 % slower.
+// One or four rows per wave: 31.2 and 32.1 us.  HBM bound: 2 reads + 2
+// writes of the row per packed row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,9 +44,13 @@ namespace pkv {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const int32_t __attribute__((address_space(4))) cint32;
 constexpr int kWavesPerGroup = 4;
 constexpr int kRowsPerWave = 2;   // rows one wave copies, all loads in flight together
-constexpr int kMaxPieces = 4;     // 16-byte pieces per lane per row (row_bytes <= 4 KB)
+constexpr int kMaxPieces = 4;     // 16-byte pieces per lane per row in the unrolled part
+constexpr int kRsrc = 0x00020000;  // gfx9-family buffer descriptor word 3
+constexpr int kLoadNT = 2;         // cache policy bits of a buffer op: non-temporal
+constexpr unsigned kOutOfRange = 0x80000000u;  // above every range used here (< 2^31)
 constexpr unsigned kErrBlock = 1u, kErrSpan = 2u, kErrCu = 4u;
 
 // 16 bytes read once: non-temporal load (global_load_dwordx4 ... nt)
@@ -41,25 +58,34 @@ __device__ __forceinline__ u32x4 load_once(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// The request of packed row r: the last b with cu[b] <= r.  Up to 63
-// requests: one load of cu per lane and a ballot; more: a binary search on
-// the scalar unit.
-__device__ __forceinline__ int request_of(const int32_t* cu, int batch, int r, int lane) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrc);
+}
+
+// p[i] through the scalar cache (p and i wave-uniform; p is read-only here)
+__device__ __forceinline__ int sload(const int32_t* p, long long i) {
+  return reinterpret_cast<cint32*>(reinterpret_cast<uintptr_t>(p))[i];
+}
+
+// The request of packed row r: the last b with cu[b] <= r, clamped to
+// [0, batch - 1].  cu_l: lane l holds cu[min(l, batch)] (used for batch < 64).
+__device__ __forceinline__ int request_of(const int32_t* cu, int batch, int r, int lane,
+                                          int cu_l) {
   if (batch < 64) {
-    const bool le = lane <= batch && cu[min(lane, batch)] <= r;
-    const unsigned long long m = __builtin_amdgcn_ballot_w64(le);
-    const int cnt = __builtin_popcountll(m);  // cu[0..cnt-1] <= r for a non-decreasing cu
-    return min(max(cnt - 1, 0), batch - 1);
+    const bool le = lane <= batch && cu_l <= r;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+    return min(max(cnt - 1, 0), batch - 1);  // cu[0..cnt-1] <= r for a non-decreasing cu
   }
   int lo = 0, hi = batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= r) lo = mid;
+    if (sload(cu, mid) <= r) lo = mid;
     else hi = mid - 1;
   }
   return lo;
 }
 
+template <int P>
 __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheWriteArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -74,77 +100,89 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void cache_write_kernel(CacheW
   const long long r0 = gw * kRowsPerWave;
   if (r0 >= a.total || a.batch <= 0) return;
 
-  // the rows' loads go out first: their source depends only on the row
-  // number, and the lookups below (cu, then start, then the table entry)
-  // are three dependent round trips that now overlap them
-  const int n16 = a.row_bytes / 16;
+  // 1. the lookup tables' first 64 entries, one per lane
+  const int cu_l = a.cu[min(lane, a.batch)];
+  const int st_l = a.start[min(lane, a.batch - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the rows' loads
+  const int rb = a.row_bytes;
   const int nrows = (int)min((long long)kRowsPerWave, a.total - r0);
-  u32x4 kx[kRowsPerWave][kMaxPieces], vx[kRowsPerWave][kMaxPieces];
+  const __amdgpu_buffer_rsrc_t ks = rsrc((const char*)a.k + r0 * rb, nrows * rb);
+  const __amdgpu_buffer_rsrc_t vs = rsrc((const char*)a.v + r0 * rb, nrows * rb);
+  unsigned piece[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int o = 16 * (lane + 64 * j);
+    piece[j] = o < rb ? (unsigned)o : kOutOfRange;
+  }
+  u32x4 kx[kRowsPerWave][P], vx[kRowsPerWave][P];
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i)
 #pragma unroll
-    for (int j = 0; j < kMaxPieces; ++j) {
-      const int c = lane + 64 * j;
-      if (i < nrows && c < n16) {
-        const long long off = (r0 + i) * a.row_bytes + 16 * c;
-        kx[i][j] = load_once((const char*)a.k + off);
-        vx[i][j] = load_once((const char*)a.v + off);
-      }
+    for (int j = 0; j < P; ++j) {
+      const unsigned o = piece[j] == kOutOfRange ? kOutOfRange : piece[j] + i * rb;
+      kx[i][j] = __builtin_amdgcn_raw_buffer_load_b128(ks, o, 0, kLoadNT);
+      vx[i][j] = __builtin_amdgcn_raw_buffer_load_b128(vs, o, 0, kLoadNT);
     }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // locate this wave's rows (uniform: scalar registers)
-  long long src[kRowsPerWave], dst[kRowsPerWave];
+  // 3. locate this wave's rows (uniform: scalar registers)
+  long long dst[kRowsPerWave];
   bool ok[kRowsPerWave];
-  int b = __builtin_amdgcn_readfirstlane(request_of(a.cu, a.batch, (int)r0, lane));
   unsigned err = 0;
+  const bool small = a.batch < 64;
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     ok[i] = false;
-    src[i] = dst[i] = 0;
+    dst[i] = 0;
     if (i >= nrows) continue;
     const int r = (int)r0 + i;
-    while (b + 1 < a.batch && a.cu[b + 1] <= r) ++b;  // rows are consecutive
-    const int c0 = a.cu[b], c1 = a.cu[b + 1];
+    const int b = __builtin_amdgcn_readfirstlane(request_of(a.cu, a.batch, r, lane, cu_l));
+    const int c0 = small ? __builtin_amdgcn_readlane(cu_l, b) : sload(a.cu, b);
+    const int c1 = small ? __builtin_amdgcn_readlane(cu_l, b + 1) : sload(a.cu, b + 1);
     if (!(c0 <= r && r < c1)) {
       err |= kErrCu;
       continue;
     }
-    const int st = a.start[b];
+    const int st = small ? __builtin_amdgcn_readlane(st_l, b) : sload(a.start, b);
     const long long p = (long long)st + (r - c0);
     if (st < 0 || p >= (long long)a.max_blocks_per_seq * a.block_size) {
       err |= kErrSpan;
       continue;
     }
-    const int pb = a.block_table[(long long)b * a.max_blocks_per_seq + p / a.block_size];
+    const int pb = sload(a.block_table, (long long)b * a.max_blocks_per_seq + p / a.block_size);
     if (pb < 0 || pb >= a.num_blocks) {
       err |= kErrBlock;
       continue;
     }
     ok[i] = true;
-    src[i] = (long long)r * a.row_bytes;
-    dst[i] = ((long long)pb * a.block_size + p % a.block_size) * a.row_bytes;
+    dst[i] = ((long long)pb * a.block_size + p % a.block_size) * rb;
   }
   if (err && a.err_flag && lane == 0) atomicOr(a.err_flag, (int)err);
 
-  // then the stores of the rows that have a slot
+  // 4. the stores; a row without a slot has an empty range
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i)
-#pragma unroll
-    for (int j = 0; j < kMaxPieces; ++j) {
-      const int c = lane + 64 * j;
-      if (ok[i] && c < n16) {
-        *reinterpret_cast<u32x4*>((char*)a.k_cache + dst[i] + 16 * c) = kx[i][j];
-        *reinterpret_cast<u32x4*>((char*)a.v_cache + dst[i] + 16 * c) = vx[i][j];
-      }
-    }
-  // rows longer than 4 KB: the rest piece by piece
   for (int i = 0; i < kRowsPerWave; ++i) {
-    if (!ok[i]) continue;
-    for (int c = lane + 64 * kMaxPieces; c < n16; c += 64) {
-      const u32x4 kv = load_once((const char*)a.k + src[i] + 16 * c);
-      const u32x4 vv = load_once((const char*)a.v + src[i] + 16 * c);
-      *reinterpret_cast<u32x4*>((char*)a.k_cache + dst[i] + 16 * c) = kv;
-      *reinterpret_cast<u32x4*>((char*)a.v_cache + dst[i] + 16 * c) = vv;
+    const __amdgpu_buffer_rsrc_t kd = rsrc((char*)a.k_cache + dst[i], ok[i] ? rb : 0);
+    const __amdgpu_buffer_rsrc_t vd = rsrc((char*)a.v_cache + dst[i], ok[i] ? rb : 0);
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      __builtin_amdgcn_raw_buffer_store_b128(kx[i][j], kd, piece[j], 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(vx[i][j], vd, piece[j], 0, 0);
+    }
+  }
+  // rows longer than 4 KB: the rest piece by piece
+  if (P == kMaxPieces) {
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (!ok[i]) continue;
+      const long long src = (r0 + i) * rb;
+      for (int c = lane + 64 * kMaxPieces; c < rb / 16; c += 64) {
+        const u32x4 kv = load_once((const char*)a.k + src + 16 * c);
+        const u32x4 vv = load_once((const char*)a.v + src + 16 * c);
+        *reinterpret_cast<u32x4*>((char*)a.k_cache + dst[i] + 16 * c) = kv;
+        *reinterpret_cast<u32x4*>((char*)a.v_cache + dst[i] + 16 * c) = vv;
+      }
     }
   }
 }
@@ -203,8 +241,13 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
   // at least one group so that cu is always checked
   const long long per_group = (long long)kWavesPerGroup * kRowsPerWave;
   const long long groups = a.total > 0 ? (a.total + per_group - 1) / per_group : 1;
-  hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)groups), dim3(kWavesPerGroup * 64), 0,
-                     stream, a);
+  const dim3 grid((unsigned)groups), block(kWavesPerGroup * 64);
+  switch (min(kMaxPieces, (a.row_bytes + 1023) / 1024)) {
+    case 1: hipLaunchKernelGGL(cache_write_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(cache_write_kernel<2>, grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(cache_write_kernel<3>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(cache_write_kernel<4>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -75,12 +75,27 @@ def test_cache_write_decode_example_slots(golden):
 
 
 @pytest.mark.parametrize("D,Hkv,bs", [(64, 1, 16), (128, 8, 16), (128, 3, 32), (64, 5, 32),
+                                     (128, 10, 16),    # 2.5 KB rows: three pieces per lane
+                                     (128, 16, 32),    # 4 KB rows: exactly the unrolled part
                                      (128, 40, 16)])   # 10 KB rows: past the 4 KB fast path
 def test_cache_write_ragged(D, Hkv, bs):
     case = workloads.make_paged_prefill(seed=3300 + D + Hkv, dtype="bf16", batch=7, num_heads=Hkv,
                                         num_kv_heads=Hkv, head_dim=D,
                                         q_lengths=[0, 1, 15, 16, 17, 100, 3],
                                         prefix=[5, 0, 1, 16, 31, 7, 0], block_size=bs, device=DEV)
+    _write_and_compare(case.k_new, case.v_new, case.cu_seq_lens_q, case.start, case.k_cache,
+                       case.v_cache, case.block_table)
+
+
+@pytest.mark.parametrize("batch", [63, 64, 300])
+def test_cache_write_many_requests(batch):
+    # from 64 requests on, a row's request is found by a binary search over
+    # cu instead of one ballot over the lanes; lengths include zeros and
+    # requests that end mid-block
+    case = workloads.make_paged_prefill(seed=3400 + batch, dtype="bf16", batch=batch, num_heads=8,
+                                        num_kv_heads=8, head_dim=128, q_lengths=("uniform", 0, 40),
+                                        prefix=("uniform", 0, 50), device=DEV)
+    assert (case.q_lengths == 0).any()
     _write_and_compare(case.k_new, case.v_new, case.cu_seq_lens_q, case.start, case.k_cache,
                        case.v_cache, case.block_table)
 
