@@ -12,7 +12,8 @@
 // 8192).  The grid-stride sweep keeps
 // every workgroup's requests inside one narrow window of the buffer at a
 // time.  The copy keeps the grid-stride form, which stays the faster one at
-// the cache write's size (83 MB: 5.1-5.2 against at most 4.75 TB/s).
+// the cache write's size (83 MB, each call after a 1 GiB buffer was
+// overwritten: 5.1-5.2 against at most 4.98 TB/s for one chunk per wave).
 // The read's words are XOR-folded and stored only if the fold hits a fixed
 // pattern, so the loads cannot be dropped and nothing is written in
 // practice.
