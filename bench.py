@@ -29,6 +29,9 @@ The same JSON line carries
   cpu_baseline    the fp64 oracle timed on the host on a bounded sample of the
                   same workload (about --cpu-seconds of work);
   warm            the same K steps back to back without flushing (wall clock);
+  write_flush     the same K steps with the cache flushed by overwriting the
+                  buffer instead of reading it (the step then also pays for
+                  writing back the dirty lines that leaves);
   s1_placement    the paged batches with contiguous blocks vs randomly
                   permuted blocks (the pages' paged-vs-contiguous comparison);
   gqa4_decode     the 64-sequence GQA-4 batch, cold;
@@ -122,6 +125,20 @@ class Flusher:
 
     def __call__(self):
         self.pkv.stream_read(self.buf, self.sink, FLUSH_WORKGROUPS, False)
+
+
+class OverwriteFlusher:
+    """The other way to flush: overwrite the 1 GiB buffer.  Reported beside
+    the headline only: it leaves the cache full of dirty lines that the
+    timed call then writes back."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
 
 
 def time_decode(pkv, torch, case, steps, warmup, flush=None):
@@ -565,6 +582,19 @@ def main():
         log("cpu baseline", res["cpu_baseline"]["value"], "GB/s on", res["cpu_baseline"]["cores"], "threads")
     else:
         res["cpu_baseline"] = None
+
+    if not args.no_extra:
+        log("the same steps with the cache flushed by overwriting 1 GiB")
+        ow = OverwriteFlusher(torch, dev)
+        tw = time_decode(pkv, torch, case, K, W, ow)
+        res["write_flush"] = {"ms_per_step": round(tw["step_ms"], 4),
+                              "gbs": round(kvb / (tw["step_ms"] * 1e-3) / 1e9, 2),
+                              "partial_kernel_ms": round(tw["part_ms"], 4),
+                              "timing": "as the headline, but the cache flushed by overwriting "
+                                        "the 1 GiB buffer: the step also writes back the dirty "
+                                        "lines that leaves"}
+        del ow
+        torch.cuda.empty_cache()
 
     if not args.no_extra and args.workload == "decode_b256_long" and args.placement == "permuted":
         n, w = max(K // 2, 5), max(W // 2, 2)
