@@ -15,8 +15,9 @@
 // order of a wave's memory traffic is what sets the time: on gfx9 the
 // vector-memory counter retires loads in issue order, so any vector load
 // issued after the rows' loads and waited on waits for all of them.  So:
-//   1. each lane loads cu[lane] and start[lane] (requests up to 63), the
-//      only vector loads besides the rows';
+//   1. each lane loads cu[lane] and start[lane] (requests up to 63): with
+//      the first waves' check of cu at the kernel's start, the only vector
+//      loads besides the rows', and issued before them;
 //   2. the rows' loads go out, all of them unconditionally, through buffer
 //      descriptors that bound them to the wave's rows (a lane past the row
 //      end gets an out-of-range offset: no memory access);
