@@ -26,11 +26,15 @@ def _bits(t):
     return workloads.to_host_bits(t)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_copy_blocks_bit_exact(dtype):
+@pytest.mark.parametrize("dtype,shape", [
+    (torch.float32, (16, 3, 128)),    # 24 KB blocks: a full and a partial 16 KB span
+    (torch.bfloat16, (16, 3, 128)),   # 12 KB: one partial span
+    (torch.float32, (32, 8, 128)),    # 128 KB: eight full spans
+])
+def test_copy_blocks_bit_exact(dtype, shape):
     gen = torch.Generator(device=DEV).manual_seed(41)
-    kc = torch.randn((12, 16, 3, 128), generator=gen, device=DEV).to(dtype)
-    vc = torch.randn((12, 16, 3, 128), generator=gen, device=DEV).to(dtype)
+    kc = torch.randn((12, *shape), generator=gen, device=DEV).to(dtype)
+    vc = torch.randn((12, *shape), generator=gen, device=DEV).to(dtype)
     src = [3, 7, 0, 11]
     dst = [5, 1, 9, 2]
     kh, vh = _bits(kc).copy(), _bits(vc).copy()

@@ -87,13 +87,14 @@ def test_cache_write_ragged(D, Hkv, bs):
                        case.v_cache, case.block_table)
 
 
-@pytest.mark.parametrize("batch", [63, 64, 300])
-def test_cache_write_many_requests(batch):
+@pytest.mark.parametrize("batch,dtype,Hkv", [(63, "bf16", 8), (64, "bf16", 8), (300, "bf16", 8),
+                                             (300, "fp32", 2)])
+def test_cache_write_many_requests(batch, dtype, Hkv):
     # from 64 requests on, a row's request is found by a binary search over
     # cu instead of one ballot over the lanes; lengths include zeros and
     # requests that end mid-block
-    case = workloads.make_paged_prefill(seed=3400 + batch, dtype="bf16", batch=batch, num_heads=8,
-                                        num_kv_heads=8, head_dim=128, q_lengths=("uniform", 0, 40),
+    case = workloads.make_paged_prefill(seed=3400 + batch, dtype=dtype, batch=batch, num_heads=Hkv,
+                                        num_kv_heads=Hkv, head_dim=128, q_lengths=("uniform", 0, 40),
                                         prefix=("uniform", 0, 50), device=DEV)
     assert (case.q_lengths == 0).any()
     _write_and_compare(case.k_new, case.v_new, case.cu_seq_lens_q, case.start, case.k_cache,
