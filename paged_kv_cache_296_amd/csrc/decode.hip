@@ -12,10 +12,15 @@
 //  * One wave64 owns one unit (sequence, partition, kv head, chunk of <= 16 q
 //    heads).  Every q head of a GQA group shares the unit's K/V bytes, so each
 //    KV byte crosses HBM once per kv head.
-//  * A 16-token tile of K is loaded straight from HBM into the A operand of
-//    v_mfma_f32_16x16x32_bf16 (lane = token, 16-byte runs of the head row);
-//    the q heads are the B operand (zero-padded to 16).  The product is S^T:
-//    each lane ends up with 4 tokens' scores for ONE q head.
+//  * A 16-token tile of K is the A operand of v_mfma_f32_16x16x32_bf16 (lane =
+//    token, 16-byte runs of the head row); the q heads are the B operand
+//    (zero-padded to 16).  The product is S^T: each lane ends up with 4
+//    tokens' scores for ONE q head.  bf16 K is loaded as whole head rows
+//    (one load instruction: 4 rows x 256 B at head_dim 128, instead of 16
+//    rows x 64 B in the operand layout) and re-laid into the operand layout
+//    through a small per-wave LDS stage right before its scores: the
+//    long-context batch 1510 -> 1480 us per step, the mixed step's decode
+//    half 1347 -> 1327 us (same box, two rounds).
 //  * P.V is computed as O^T = V^T P^T with v_mfma_f32_16x16x16_bf16: the P^T
 //    operand is exactly the S^T accumulator layout, so scores never move
 //    between lanes, and the O^T accumulator of a lane also belongs to that
@@ -150,13 +155,13 @@ __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t r, int voff, int s
 // access to the block.  koff/voff are the lane's loop-invariant offsets.
 template <bool BF16, class S, int CPOL>
 __device__ __forceinline__ void load_tile(Tile<BF16, S>& r, const char* tk, const char* tv,
-                                          int bytes, int koff, int voff, int tok) {
+                                          int bytes, int koff, int kstep, int voff, int tok) {
   using W = Words<BF16>;
   const __amdgpu_buffer_rsrc_t rk = rsrc(tk, bytes), rv = rsrc(tv, bytes);
 #pragma unroll
   for (int t = 0; t < S::NKL; ++t)
     r.k[t] = __builtin_bit_cast(typename W::vec,
-                                __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * t, 0, CPOL));
+                                __builtin_amdgcn_raw_buffer_load_b128(rk, koff + kstep * t, 0, CPOL));
 #pragma unroll
   for (int i = 0; i < 4; ++i) load_v<BF16, S, CPOL>(rv, voff, i * tok, r.v[i]);
 }
@@ -312,8 +317,8 @@ __device__ __forceinline__ void store_out(char* dst, const float* o) {
 // unit's last tiles to complete before the next ticket exchange needs it.
 template <bool BF16, int D, int BS, int CPOL, class Started>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, float* run_w,
-                                            int lane, int seq, int p0, int nparts, int L, int kvh,
-                                            int hc, Started&& started) {
+                                            char* kst, int lane, int seq, int p0, int nparts,
+                                            int L, int kvh, int hc, Started&& started) {
   using S = Shape<BF16, D>;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int P = a.part_tokens;
@@ -497,14 +502,43 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
   const int last = ntiles - 1;
   const int nvalid_last = tend - (tb + 16 * last);
   const int tpp = P / 16;  // tiles per partition (P is a multiple of 16)
-  const int koff = r16 * tok + 16 * q4;
+  // K: bf16 tiles are loaded as whole token rows (each load instruction
+  // covers 64 / LPR rows of LPR 16-byte pieces: 4 rows of 256 B at head_dim
+  // 128) and re-laid into the MFMA operand layout (lane = token, 64-byte
+  // steps along the row) through the wave's LDS stage just before their
+  // scores are taken; fp32 tiles are loaded in the operand layout directly
+  constexpr int LPR = S::ROW / 16;  // lanes per token row
+  constexpr bool ROWK = BF16 && LPR <= 64 && 64 % LPR == 0;
+  constexpr int KPITCH = S::ROW + 16;  // LDS bytes per staged row (padded against bank conflicts)
+  const int koff = ROWK ? (lane / LPR) * tok + 16 * (lane % LPR) : r16 * tok + 16 * q4;
+  const int kstep = ROWK ? (64 / LPR) * tok : 64;
+  auto relayout = [&](Tile<BF16, S>& r) __attribute__((always_inline)) {
+    if constexpr (ROWK) {
+      using V = typename Words<BF16>::vec;
+#pragma unroll
+      for (int t = 0; t < S::NKL; ++t)
+        *reinterpret_cast<V*>(kst + ((64 / LPR) * t + lane / LPR) * KPITCH + 16 * (lane % LPR)) =
+            r.k[t];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < S::NKL; ++t)
+        r.k[t] = *reinterpret_cast<const V*>(kst + r16 * KPITCH + 64 * t + 16 * q4);
+      // the next tile's writes must not overtake these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  };
   const int voff = 4 * q4 * tok + r16 * (S::E * S::ESZ);
 
   auto issue = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
     const int pb = __builtin_amdgcn_readfirstlane(slice_w[(16 * t) / BS]);
     const int inblk = (16 * t) % BS;
     const long long off = (long long)pb * blk + (long long)inblk * tok;
-    load_tile<BF16, S, CPOL>(r, kbase + off, vbase + off, (BS - inblk) * tok, koff, voff, tok);
+    load_tile<BF16, S, CPOL>(r, kbase + off, vbase + off, (BS - inblk) * tok, koff, kstep, voff,
+                             tok);
   };
   // a partition ends after tile t: write its partial (the run's last
   // partition is written after the loop)
@@ -512,11 +546,13 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* slice_w, f
     if ((t + 1) % tpp == 0 && t != last) flush(p0 + t / tpp);
   };
   auto compute_full = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
+    relayout(r);
     tile_update<BF16, S, false>(r, tile_scores<BF16, S>(r, qr), 16, lane, a.scale_log2, m_run,
                                 l_run, acc);
     boundary(t);
   };
   auto compute = [&](int t, Tile<BF16, S>& r) __attribute__((always_inline)) {
+    if (t == last) relayout(r);
     if (t == last)
       tile_update<BF16, S, true>(r, tile_scores<BF16, S>(r, qr), nvalid_last, lane, a.scale_log2,
                                  m_run, l_run, acc);
@@ -590,6 +626,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF1
 void decode_partial_kernel(DecodeArgs a) {
   __shared__ int slice[kWaves][kMaxSlice];
   __shared__ float run_state[kWaves][(D / 4 + 2) * 64];  // per lane: D/4 sums, m, l
+  __shared__ __attribute__((aligned(16))) char kstage[kWaves][BF16 ? 16 * (D * 2 + 16) : 16];
   const int lane = threadIdx.x & 63;
   // the wave index is uniform; saying so keeps everything derived from it
   // (unit, kv head, block bases, buffer descriptors) in scalar registers
@@ -614,7 +651,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int4 item = a.items[u / (unsigned)per_item];
     const int r = (int)(u % (unsigned)per_item);
     const int packed = __builtin_amdgcn_readfirstlane(item.y);
-    decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane,
+    decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], kstage[wave], lane,
                              __builtin_amdgcn_readfirstlane(item.x),
                              packed >> 8, packed & 255, __builtin_amdgcn_readfirstlane(item.z),
                              r / a.head_chunks, r % a.head_chunks, [&]() {
@@ -632,6 +669,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(BF1
 void decode_direct_kernel(DecodeArgs a) {
   __shared__ int slice[kWaves][kMaxSlice];
   __shared__ float run_state[kWaves][(D / 4 + 2) * 64];
+  __shared__ __attribute__((aligned(16))) char kstage[kWaves][BF16 ? 16 * (D * 2 + 16) : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   unsigned unit = blockIdx.x * kWaves + wave;
@@ -646,8 +684,8 @@ void decode_direct_kernel(DecodeArgs a) {
   const int Lp = L + a.has_new;
   const bool bad = L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS;
   if (part > 0 && (bad || part * a.part_tokens >= Lp)) return;
-  decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], lane, seq, part, 1, L, kvh,
-                                        hc, []() {});
+  decode_unit<BF16, D, BS, kCpolStream>(a, slice[wave], run_state[wave], kstage[wave], lane, seq,
+                                        part, 1, L, kvh, hc, []() {});
 }
 
 // Work list for the persistent kernel, one workgroup.  Every sequence's
