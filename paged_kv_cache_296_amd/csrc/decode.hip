@@ -869,7 +869,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       *reinterpret_cast<f32x4*>(dst) = o;
   };
 
+  // the run length and the sequence's length are both requested before
+  // either is used, so that the two round trips overlap (the control words
+  // always exist; the direct grid leaves them unset and does not use them)
+  const int R_plan = a.ctrl[2];
   const int L = a.cache_seqlens[seq];
+  asm volatile("" ::"s"(R_plan), "v"(L));
   const int Lp = L + a.has_new;
   if (L < 0 || (long long)Lp > (long long)a.max_blocks_per_seq * BS) {
     const float nan = __builtin_nanf("");
@@ -878,7 +883,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
   const int np = Lp > 0 ? (Lp + a.part_tokens - 1) / a.part_tokens : 1;
   // each run of R partitions left one partial, at its first slot
-  const int R = a.direct ? 1 : a.ctrl[2];
+  const int R = a.direct ? 1 : R_plan;
   const int nruns = (np + R - 1) / R;
   const long long blk0 = sk * a.n_parts;
   const float* accp = a.ws_acc + blk0 * a.group * D + 16 * hc * D + 4 * t;
