@@ -320,6 +320,23 @@ def test_runs_of_partitions(pt):
     run_case(case, "bf16")
 
 
+@pytest.mark.parametrize("D,bs", [(64, 16), (64, 32), (128, 32)])
+def test_runs_of_partitions_other_shapes(D, bs):
+    """The persistent kernel with runs of several partitions at the other
+    head sizes and block sizes: bf16 K is loaded as whole head rows (8 rows
+    of 128 B per load at head_dim 64, 4 of 256 B at 128) and re-laid into
+    the operand layout in LDS, and a 32-token block holds two tiles."""
+    lengths = np.random.default_rng(D + bs).integers(1, 1500, size=96)
+    lengths[:6] = [32, 64, 96, 1024, 1023, 1]
+    case = workloads.make_decode(seed=7500 + D + bs, dtype="bf16", batch=96, num_heads=16,
+                                 num_kv_heads=8, head_dim=D, block_size=bs,
+                                 lengths=lengths.tolist(), num_blocks=12000, append=True,
+                                 partition_tokens=32, device=DEV)
+    units = int(sum((int(L) + 1 + 31) // 32 for L in lengths)) * 8
+    assert units > 2 * 3 * 1024  # beyond the direct grid's limit: the persistent kernel runs
+    run_case(case, "bf16")
+
+
 def test_work_list_past_the_cached_chunks():
     """4500 sequences: the plan kernel keeps the lengths of the first 4096
     (four chunks of 1024) in registers between its passes and reads the rest
